@@ -1,0 +1,191 @@
+#!/usr/bin/env python3
+"""Benchmark of the Hadamard-rotated W4A4 prompt GEMM on one MI355X.
+
+A step is one pass of the route over one batch: quantize_act_h32 (FWHT-32 +
+4-bit quantization of the activations) then w4a4_gemm, on the dense
+attention projection at 512 prompt tokens (M=512, K=5120, N=5120, bf16
+activations).  Inputs are resident in HBM before the timed region; each step
+uses a different copy of the weights and activations, cycling through enough
+copies (>= 512 MB) that the 256 MB last-level cache cannot hold them.
+
+Prints ONE JSON line.  `value` is prompt tokens per second of the step.  The
+`roofline` object covers the GEMM kernel (the dominant kernel): its average
+duration is measured with HIP events recorded on the launch stream around
+every GEMM in the timed region.  `cpu_baseline` times the CPU oracle on the
+same workload (test infrastructure, not the product path).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+# MI355X published peaks
+PEAK_INT8_OPS = 5.0e15          # dense int8 MFMA, ops/s
+PEAK_HBM = 8.0e12               # bytes/s
+# fp32 VALU issue rate with packed fp32 instructions disabled:
+# 256 CU x 4 SIMD x 16 lanes x 2.4 GHz = 39.3e12 lane-ops/s
+PEAK_VALU_OPS = 256 * 4 * 16 * 2.4e9
+
+WORKLOADS = {
+    "attn512": dict(m=512, k=5120, n=5120, key="x"),
+    "long1024": dict(m=1024, k=5120, n=17408, key="x"),
+    "m16_gate": dict(m=16, k=5120, n=17408, key="x"),
+    "m16_down": dict(m=16, k=17408, n=5120, key="x"),
+    "m16_attn": dict(m=16, k=5120, n=5120, key="x"),
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="attn512", choices=sorted(WORKLOADS))
+    ap.add_argument("--bits", type=int, default=4, choices=(4, 8))
+    ap.add_argument("--cold-bytes", type=float, default=512e6,
+                    help="total bytes of distinct input copies cycled through")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    return ap.parse_args()
+
+
+def gemm_bytes(m, k, n, bits):
+    """Algorithmic HBM bytes of one GEMM: weight image, codes, scales, fp32 output."""
+    return n * k * 18 // 32 + m * k * bits // 8 + m * (k // 32) * 4 + m * n * 4
+
+
+def cpu_baseline(data, wl, bits, seconds):
+    import oracle
+    x = data[wl["key"]]
+    m, k, n = wl["m"], wl["k"], wl["n"]
+    w, dw = oracle.q4_0_decode(data["w"], k)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        q, d, _ = oracle.quantize(x, bits)
+        oracle.gemm_rect(q, d, w, dw, 0, m, 0, n)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or reps >= 50:
+            break
+    return {"value": reps * m / el, "unit": "tokens/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": "whole %s workload (quantize %dx%d + %dx%dx%d GEMM, fp64 output), "
+                      "%d repetition(s) in %.1f s" % (wl_name_of(wl), m, k, m, k, n, reps, el)}
+
+
+def wl_name_of(wl):
+    for name, v in WORKLOADS.items():
+        if v is wl:
+            return name
+    return "?"
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from bit_prefill_gemm_amd import binding as bb
+    from bit_prefill_gemm_amd import synth
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    bb.lib()
+    wl = WORKLOADS[args.workload]
+    m, k, n, bits = wl["m"], wl["k"], wl["n"], args.bits
+    data = synth.make(args.workload)
+    x_host = data[wl["key"]]
+    W0 = bb.rotate_pack_weights(data["w"], bb.SRC_Q4_0_ROTATED, n, k)
+
+    dev = torch.device("cuda:0")
+    x0 = torch.from_numpy(x_host.view(np.int16)).to(dev).view(torch.bfloat16)
+    img0 = torch.from_numpy(W0.image).to(dev)
+    per_copy = img0.numel() + x0.numel() * 2
+    copies = max(1, int(math.ceil(args.cold_bytes / per_copy)))
+    imgs = [img0] + [img0.clone() for _ in range(copies - 1)]
+    xs = [x0] + [x0.clone() for _ in range(copies - 1)]
+    Ws = [bb.Weights(W0.desc, im) for im in imgs]
+    codes = torch.empty((m, k // 2 if bits == 4 else k), dtype=torch.uint8, device=dev)
+    scales = torch.empty((m, k // 32), dtype=torch.float32, device=dev)
+    y = torch.empty((m, n), dtype=torch.float32, device=dev)
+    stream = torch.cuda.Stream(device=dev)
+
+    def step(i, ev=None):
+        j = i % copies
+        bb.quantize_act_h32(xs[j], bits, codes=codes, scales=scales, stream=stream)
+        if ev is not None:
+            ev[0].record(stream)
+        bb.w4a4_gemm(codes, scales, bits, Ws[j], y=y, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+
+    with torch.cuda.stream(stream):
+        for i in range(args.warmup):
+            step(i)
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step(args.warmup + i, evs[i])
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    gemm_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    gemm_s = gemm_ms * 1e-3
+    ops = 2.0 * m * n * k
+    eff_tops = ops / gemm_s / 1e12
+    # the fp32 epilogue: two VALU operations per (m, n, 32-block)
+    epi_ops = 2.0 * m * n * (k // 32)
+    gbytes = gemm_bytes(m, k, n, bits)
+
+    out = {
+        "metric": "prompt tokens/s + effective TOPS (% int8 MFMA peak) for rotated W4A4 GEMM, M=512",
+        "value": m / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i8" if bits == 8 else "i4 (i8 MFMA operands, fp32 block-scale epilogue)",
+        "data": "synthetic",
+        "config": {"workload": "%s: M=%d K=%d N=%d, bf16 activations, rotated Q4_0 weights, "
+                               "%d-bit activation codes" % (args.workload, m, k, n, bits),
+                   "m": m, "k": k, "n": n, "act_bits": bits, "cold_copies": copies},
+        "roofline": {"bound": "mfma", "achieved": eff_tops, "peak": PEAK_INT8_OPS / 1e12,
+                     "unit": "TOP/s (int8)", "frac": eff_tops / (PEAK_INT8_OPS / 1e12),
+                     "traffic": None},
+        "gemm_us": gemm_ms * 1e3,
+        "step_us": ms_per_step * 1e3,
+        "eff_TOPS": eff_tops,
+        "pct_int8_peak": 100.0 * eff_tops / (PEAK_INT8_OPS / 1e12),
+        "gemm_hbm_GBps": gbytes / gemm_s / 1e9,
+        "pct_hbm": 100.0 * gbytes / gemm_s / PEAK_HBM,
+        "epilogue_valu_frac": epi_ops / gemm_s / PEAK_VALU_OPS,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(data, wl, bits, args.cpu_seconds)
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,214 @@
+"""Thin Python binding over libbpg.so (the C ABI in include/bpg.h).
+
+Argument marshalling only: every step of the route runs in the library's HIP
+kernels (or, for rotate_pack_weights, in its host code).  PyTorch provides
+device memory and streams.  If the library has not been built, the first call
+raises; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libbpg.so")
+
+BPG_OK = 0
+STATUS_NAMES = {0: "BPG_OK", 1: "BPG_ERR_NULL", 2: "BPG_ERR_SHAPE", 3: "BPG_ERR_ALIGN",
+                4: "BPG_ERR_DTYPE", 5: "BPG_ERR_STAMP", 6: "BPG_ERR_BUFFER",
+                7: "BPG_ERR_DEVICE", 8: "BPG_ERR_LAUNCH"}
+
+SRC_F32, SRC_BF16, SRC_Q4_0_ROTATED = 0, 1, 2
+X_F32, X_BF16 = 0, 1
+
+ENTRY_POINTS = ("bpg_status_str", "rotate_pack_weights_bytes", "rotate_pack_weights",
+                "quantize_act_h32", "w4a4_gemm", "w4a4_grouped_gemm", "w4a4_gemm_blocksums")
+
+
+class WeightsDesc(ctypes.Structure):
+    _fields_ = [("magic", ctypes.c_uint32), ("version", ctypes.c_uint32),
+                ("rotation", ctypes.c_uint32), ("layout", ctypes.c_uint32),
+                ("n", ctypes.c_int64), ("k", ctypes.c_int64), ("num_experts", ctypes.c_int64),
+                ("bytes", ctypes.c_uint64), ("scales_offset", ctypes.c_uint64)]
+
+
+class BpgError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__("%s: %s (%s)" % (where, STATUS_NAMES.get(status, str(status)),
+                                          _lib_handle().bpg_status_str(status).decode()))
+
+
+_lib = None
+_i64 = ctypes.c_int64
+_vp = ctypes.c_void_p
+
+
+def _lib_handle():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError("libbpg.so is not built (run __graft_entry__.build() or "
+                           "python bit_prefill_gemm_amd/build.py); there is no fallback path")
+    lib = ctypes.CDLL(LIB_PATH)
+    lib.bpg_status_str.restype = ctypes.c_char_p
+    lib.bpg_status_str.argtypes = [ctypes.c_int]
+    lib.rotate_pack_weights_bytes.restype = ctypes.c_size_t
+    lib.rotate_pack_weights_bytes.argtypes = [_i64, _i64, _i64]
+    lib.rotate_pack_weights.restype = ctypes.c_int
+    lib.rotate_pack_weights.argtypes = [_vp, ctypes.c_int, _i64, _i64, _i64, _vp, ctypes.c_size_t,
+                                        ctypes.POINTER(WeightsDesc)]
+    lib.quantize_act_h32.restype = ctypes.c_int
+    lib.quantize_act_h32.argtypes = [_vp, ctypes.c_int, _i64, _i64, _i64, ctypes.c_int, _vp, _vp,
+                                     _vp]
+    lib.w4a4_gemm.restype = ctypes.c_int
+    lib.w4a4_gemm.argtypes = [_vp, _vp, ctypes.c_int, _i64, ctypes.POINTER(WeightsDesc), _vp, _vp,
+                              _i64, _vp]
+    lib.w4a4_grouped_gemm.restype = ctypes.c_int
+    lib.w4a4_grouped_gemm.argtypes = [_vp, _vp, ctypes.c_int, _i64, _vp,
+                                      ctypes.POINTER(WeightsDesc), _vp, _vp, _i64, _vp]
+    lib.w4a4_gemm_blocksums.restype = ctypes.c_int
+    lib.w4a4_gemm_blocksums.argtypes = [_vp, _vp, ctypes.c_int, _i64,
+                                        ctypes.POINTER(WeightsDesc), _vp, _i64, _i64, _i64, _i64,
+                                        _i64, _vp, _vp]
+    _lib = lib
+    return lib
+
+
+def lib():
+    """The loaded ctypes library (raises if it is not built)."""
+    return _lib_handle()
+
+
+def _check(status: int, where: str):
+    if status != BPG_OK:
+        raise BpgError(status, where)
+
+
+# ------------------------------------------------------------------ helpers
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream_handle(stream):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+class Weights:
+    """A packed weight image on the device plus its stamp."""
+
+    def __init__(self, desc: WeightsDesc, image):
+        self.desc = desc
+        self.image = image  # torch uint8 tensor on the device (or numpy on the host)
+
+    @property
+    def n(self):
+        return self.desc.n
+
+    @property
+    def k(self):
+        return self.desc.k
+
+    @property
+    def num_experts(self):
+        return self.desc.num_experts
+
+    def to(self, device):
+        torch = _torch()
+        img = self.image
+        if isinstance(img, np.ndarray):
+            img = torch.from_numpy(img)
+        return Weights(self.desc, img.to(device))
+
+
+# ------------------------------------------------------------------ entry points
+
+def rotate_pack_weights_bytes(n: int, k: int, num_experts: int = 1) -> int:
+    return int(_lib_handle().rotate_pack_weights_bytes(n, k, num_experts))
+
+
+def rotate_pack_weights(src: np.ndarray, kind: int, n: int, k: int,
+                        num_experts: int = 1) -> Weights:
+    """Host-side packing; returns Weights with a numpy image (call .to(device))."""
+    src = np.ascontiguousarray(src)
+    nbytes = rotate_pack_weights_bytes(n, k, num_experts)
+    if nbytes == 0:
+        raise BpgError(2, "rotate_pack_weights")
+    img = np.empty(nbytes, dtype=np.uint8)
+    desc = WeightsDesc()
+    st = _lib_handle().rotate_pack_weights(src.ctypes.data_as(_vp), kind, n, k, num_experts,
+                                           img.ctypes.data_as(_vp), img.nbytes,
+                                           ctypes.byref(desc))
+    _check(st, "rotate_pack_weights")
+    return Weights(desc, img)
+
+
+def quantize_act_h32(x, act_bits: int = 4, codes=None, scales=None, stream=None):
+    """x: 2-D cuda tensor (float32 or bfloat16, unit stride along K).  Returns (codes, scales)."""
+    torch = _torch()
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be a 2-D tensor with unit stride along K")
+    dt = {torch.float32: X_F32, torch.bfloat16: X_BF16}.get(x.dtype)
+    if dt is None:
+        raise TypeError("x must be float32 or bfloat16")
+    m, k = x.shape
+    if codes is None:
+        codes = torch.empty((m, k // 2 if act_bits == 4 else k), dtype=torch.uint8,
+                            device=x.device)
+    if scales is None:
+        scales = torch.empty((m, k // 32), dtype=torch.float32, device=x.device)
+    st = _lib_handle().quantize_act_h32(_dptr(x), dt, m, k, x.stride(0), act_bits, _dptr(codes),
+                                        _dptr(scales), _stream_handle(stream))
+    _check(st, "quantize_act_h32")
+    return codes, scales
+
+
+def w4a4_gemm(codes, scales, act_bits: int, w: Weights, y=None, stream=None):
+    torch = _torch()
+    m = codes.shape[0]
+    if y is None:
+        y = torch.empty((m, w.n), dtype=torch.float32, device=codes.device)
+    st = _lib_handle().w4a4_gemm(_dptr(codes), _dptr(scales), act_bits, m,
+                                 ctypes.byref(w.desc), _dptr(w.image), _dptr(y), y.stride(0),
+                                 _stream_handle(stream))
+    _check(st, "w4a4_gemm")
+    return y
+
+
+def w4a4_grouped_gemm(codes, scales, act_bits: int, expert_offsets, w: Weights, y=None,
+                      stream=None):
+    torch = _torch()
+    rows = codes.shape[0]
+    if y is None:
+        y = torch.empty((rows, w.n), dtype=torch.float32, device=codes.device)
+    st = _lib_handle().w4a4_grouped_gemm(_dptr(codes), _dptr(scales), act_bits, rows,
+                                         _dptr(expert_offsets), ctypes.byref(w.desc),
+                                         _dptr(w.image), _dptr(y), y.stride(0),
+                                         _stream_handle(stream))
+    _check(st, "w4a4_grouped_gemm")
+    return y
+
+
+def w4a4_gemm_blocksums(codes, scales, act_bits: int, w: Weights, m0: int, m1: int, n0: int,
+                        n1: int, expert: int = 0, sums=None, stream=None):
+    torch = _torch()
+    m = codes.shape[0]
+    if sums is None:
+        sums = torch.empty((m1 - m0, n1 - n0, w.k // 32), dtype=torch.int32, device=codes.device)
+    st = _lib_handle().w4a4_gemm_blocksums(_dptr(codes), _dptr(scales), act_bits, m,
+                                           ctypes.byref(w.desc), _dptr(w.image), expert, m0, m1,
+                                           n0, n1, _dptr(sums), _stream_handle(stream))
+    _check(st, "w4a4_gemm_blocksums")
+    return sums

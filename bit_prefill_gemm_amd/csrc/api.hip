@@ -1,0 +1,390 @@
+// api.hip -- the C ABI declared in include/bpg.h.
+//
+// Every entry point validates its arguments and the weight stamp on the host
+// first (so each error except DEVICE / LAUNCH is reported without touching a
+// GPU), then checks that the current device is a gfx950, then enqueues its
+// kernels on the caller's stream.  rotate_pack_weights runs on the CPU only.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstring>
+
+#include "bpg.h"
+#include "internal.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_device_ok[kMaxDevices]; // 0 unknown, 1 gfx950, 2 other
+
+bpg_status check_device()
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0)
+        return BPG_ERR_DEVICE;
+    if (dev < kMaxDevices) {
+        int s = g_device_ok[dev].load(std::memory_order_relaxed);
+        if (s == 1)
+            return BPG_OK;
+        if (s == 2)
+            return BPG_ERR_DEVICE;
+    }
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess)
+        return BPG_ERR_DEVICE;
+    const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    if (dev < kMaxDevices)
+        g_device_ok[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
+    return ok ? BPG_OK : BPG_ERR_DEVICE;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bpg_status launch_status(hipError_t e) { return e == hipSuccess ? BPG_OK : BPG_ERR_LAUNCH; }
+
+uint64_t image_bytes(int64_t n, int64_t k, int64_t e)
+{
+    return (uint64_t)e * (uint64_t)n * (uint64_t)(k / 32) * 18u;
+}
+
+uint64_t scales_offset(int64_t n, int64_t k, int64_t e)
+{
+    return (uint64_t)e * (uint64_t)n * (uint64_t)(k / 32) * 16u;
+}
+
+bool shape_ok(int64_t n, int64_t k, int64_t e)
+{
+    if (n <= 0 || k <= 0 || e <= 0 || n % 32 != 0 || k % 32 != 0)
+        return false;
+    // keep every byte offset of the image inside int64 and every tile count in int
+    if (n > (int64_t)1 << 30 || k > (int64_t)1 << 30 || e > (int64_t)1 << 20)
+        return false;
+    const long double bytes = (long double)e * n * (k / 32) * 18;
+    return bytes < (long double)((uint64_t)1 << 62);
+}
+
+// The stamp check: the analogue of refusing a file that is not a rotated one
+// ("509 tokens a second of prompt: the Hadamard route ships", section "Making
+// the file is part of the engine").
+bpg_status check_stamp(const bpg_weights_desc *w)
+{
+    if (w->magic != BPG_WEIGHTS_MAGIC || w->version != BPG_WEIGHTS_VERSION ||
+        w->rotation != 32 || w->layout != BPG_LAYOUT_COLTILE32)
+        return BPG_ERR_STAMP;
+    if (!shape_ok(w->n, w->k, w->num_experts))
+        return BPG_ERR_STAMP;
+    if (w->bytes != image_bytes(w->n, w->k, w->num_experts) ||
+        w->scales_offset != scales_offset(w->n, w->k, w->num_experts))
+        return BPG_ERR_STAMP;
+    return BPG_OK;
+}
+
+bpg_status check_act(const void *codes, const float *scales, int act_bits, int64_t rows,
+                     int64_t k)
+{
+    if (act_bits != 4 && act_bits != 8)
+        return BPG_ERR_DTYPE;
+    if (rows < 0 || rows > ((int64_t)1 << 31) - 1)
+        return BPG_ERR_SHAPE;
+    if (!codes || !scales)
+        return BPG_ERR_NULL;
+    if (!aligned16(codes) || !aligned16(scales))
+        return BPG_ERR_ALIGN;
+    (void)k;
+    return BPG_OK;
+}
+
+// ---------------------------------------------------------------- host packer
+
+// fp64 -> fp16 bits, round to nearest even (the compiler's conversion through
+// _Float16 is IEEE round-to-nearest-even on this host).
+uint16_t f64_to_f16_bits(double v)
+{
+    _Float16 h = (_Float16)v;
+    uint16_t b;
+    std::memcpy(&b, &h, 2);
+    return b;
+}
+
+double f16_bits_to_f64(uint16_t b)
+{
+    _Float16 h;
+    std::memcpy(&h, &b, 2);
+    return (double)h;
+}
+
+// In-place fp64 Walsh-Hadamard butterflies, stages h = 1..16, then times
+// fp64 1/sqrt(32) ("509 tokens a second of prompt: the Hadamard route ships",
+// section "The rotation": the weights get the same transform, once, offline).
+void rotate_block_f64(double v[32])
+{
+    for (int h = 1; h < 32; h <<= 1)
+        for (int j = 0; j < 32; j++)
+            if ((j & h) == 0) {
+                const double a = v[j], b = v[j + h];
+                v[j] = a + b;
+                v[j + h] = a - b;
+            }
+    const double c = std::sqrt(2.0) / 8.0;
+    for (int i = 0; i < 32; i++)
+        v[i] = v[i] * c;
+}
+
+// One rotated Q4_0 block from 32 unrotated float weights.
+void quantize_weight_block(const double in[32], uint8_t blk[18])
+{
+    double v[32];
+    std::memcpy(v, in, sizeof v);
+    rotate_block_f64(v);
+    double amax = 0.0;
+    for (int i = 0; i < 32; i++)
+        amax = std::fabs(v[i]) > amax ? std::fabs(v[i]) : amax;
+    const uint16_t hb = f64_to_f16_bits(amax / 7.0);
+    const double dw = f16_bits_to_f64(hb);
+    blk[0] = (uint8_t)(hb & 0xFF);
+    blk[1] = (uint8_t)(hb >> 8);
+    int u[32];
+    for (int i = 0; i < 32; i++) {
+        double q = dw == 0.0 ? 0.0 : std::nearbyint(v[i] / dw);
+        q = q < -8.0 ? -8.0 : (q > 7.0 ? 7.0 : q);
+        u[i] = (int)q + 8;
+    }
+    for (int j = 0; j < 16; j++)
+        blk[2 + j] = (uint8_t)(u[j] | (u[j + 16] << 4));
+}
+
+// Place one canonical 18-byte block of (expert e, row n, block b) in the image.
+inline void place_block(const uint8_t blk[18], int64_t e, int64_t n, int64_t b, int64_t N,
+                        int64_t B, uint8_t *codes, uint16_t *scales)
+{
+    const int64_t t = (e * (N / 32) + n / 32) * B + b; // (expert, column tile, block)
+    std::memcpy(codes + (t * 32 + n % 32) * 16, blk + 2, 16);
+    scales[t * 32 + n % 32] = (uint16_t)(blk[0] | (blk[1] << 8));
+}
+
+} // namespace
+
+extern "C" {
+
+const char *bpg_status_str(bpg_status s)
+{
+    switch (s) {
+    case BPG_OK: return "ok";
+    case BPG_ERR_NULL: return "null pointer";
+    case BPG_ERR_SHAPE: return "invalid shape";
+    case BPG_ERR_ALIGN: return "misaligned pointer or leading dimension";
+    case BPG_ERR_DTYPE: return "unsupported dtype, source kind or act_bits";
+    case BPG_ERR_STAMP: return "weight image stamp missing, foreign, unrotated or inconsistent";
+    case BPG_ERR_BUFFER: return "destination buffer too small";
+    case BPG_ERR_DEVICE: return "current device is not a gfx950 GPU";
+    case BPG_ERR_LAUNCH: return "kernel launch failed";
+    }
+    return "unknown status";
+}
+
+size_t rotate_pack_weights_bytes(int64_t n, int64_t k, int64_t num_experts)
+{
+    if (!shape_ok(n, k, num_experts))
+        return 0;
+    return (size_t)image_bytes(n, k, num_experts);
+}
+
+bpg_status rotate_pack_weights(const void *src, bpg_src_kind kind, int64_t n, int64_t k,
+                               int64_t num_experts, void *dst_host, size_t dst_bytes,
+                               bpg_weights_desc *desc_out)
+{
+    if (kind != BPG_SRC_F32 && kind != BPG_SRC_BF16 && kind != BPG_SRC_Q4_0_ROTATED)
+        return BPG_ERR_DTYPE;
+    if (!shape_ok(n, k, num_experts))
+        return BPG_ERR_SHAPE;
+    if (!src || !dst_host || !desc_out)
+        return BPG_ERR_NULL;
+    const uint64_t total = image_bytes(n, k, num_experts);
+    if (dst_bytes < total)
+        return BPG_ERR_BUFFER;
+
+    const int64_t B = k / 32;
+    uint8_t *codes = static_cast<uint8_t *>(dst_host);
+    uint16_t *scales = reinterpret_cast<uint16_t *>(codes + scales_offset(n, k, num_experts));
+    for (int64_t e = 0; e < num_experts; e++)
+        for (int64_t r = 0; r < n; r++)
+            for (int64_t b = 0; b < B; b++) {
+                uint8_t blk[18];
+                const int64_t row = e * n + r;
+                if (kind == BPG_SRC_Q4_0_ROTATED) {
+                    std::memcpy(blk, static_cast<const uint8_t *>(src) + (row * B + b) * 18, 18);
+                } else {
+                    double in[32];
+                    for (int i = 0; i < 32; i++) {
+                        const int64_t idx = row * k + b * 32 + i;
+                        if (kind == BPG_SRC_F32) {
+                            in[i] = (double)static_cast<const float *>(src)[idx];
+                        } else {
+                            const uint32_t bits = (uint32_t)static_cast<const uint16_t *>(src)[idx] << 16;
+                            float f;
+                            std::memcpy(&f, &bits, 4);
+                            in[i] = (double)f;
+                        }
+                    }
+                    quantize_weight_block(in, blk);
+                }
+                place_block(blk, e, r, b, n, B, codes, scales);
+            }
+
+    bpg_weights_desc d;
+    std::memset(&d, 0, sizeof d);
+    d.magic = BPG_WEIGHTS_MAGIC;
+    d.version = BPG_WEIGHTS_VERSION;
+    d.rotation = 32;
+    d.layout = BPG_LAYOUT_COLTILE32;
+    d.n = n;
+    d.k = k;
+    d.num_experts = num_experts;
+    d.bytes = total;
+    d.scales_offset = scales_offset(n, k, num_experts);
+    *desc_out = d;
+    return BPG_OK;
+}
+
+bpg_status quantize_act_h32(const void *x, bpg_x_dtype dt, int64_t m, int64_t k, int64_t ldx,
+                            int act_bits, void *codes, float *scales, void *stream)
+{
+    if (dt != BPG_X_F32 && dt != BPG_X_BF16)
+        return BPG_ERR_DTYPE;
+    if (act_bits != 4 && act_bits != 8)
+        return BPG_ERR_DTYPE;
+    if (m < 0 || k <= 0 || k % 32 != 0 || ldx < k || m > ((int64_t)1 << 31) - 1 ||
+        k > ((int64_t)1 << 30) || ldx > ((int64_t)1 << 40))
+        return BPG_ERR_SHAPE;
+    if (!x || !codes || !scales)
+        return BPG_ERR_NULL;
+    if (!aligned16(x) || !aligned16(codes) || !aligned16(scales) || ldx % 4 != 0)
+        return BPG_ERR_ALIGN;
+    bpg_status s = check_device();
+    if (s != BPG_OK)
+        return s;
+    return launch_status(bpg::launch_quantize(x, (int)dt, m, k, ldx, act_bits, 1, codes, scales,
+                                              static_cast<hipStream_t>(stream)));
+}
+
+bpg_status w4a4_gemm(const void *codes, const float *scales, int act_bits, int64_t m,
+                     const bpg_weights_desc *w, const void *w_dev, float *y, int64_t ldy,
+                     void *stream)
+{
+    if (!w)
+        return BPG_ERR_NULL;
+    bpg_status s = check_stamp(w);
+    if (s != BPG_OK)
+        return s;
+    if (w->num_experts != 1)
+        return BPG_ERR_STAMP;
+    s = check_act(codes, scales, act_bits, m, w->k);
+    if (s != BPG_OK)
+        return s;
+    if (ldy < w->n)
+        return BPG_ERR_SHAPE;
+    if (!w_dev || !y)
+        return BPG_ERR_NULL;
+    if (!aligned16(w_dev) || !aligned16(y) || ldy % 4 != 0)
+        return BPG_ERR_ALIGN;
+    s = check_device();
+    if (s != BPG_OK)
+        return s;
+    bpg::GemmProblem p{};
+    p.codes = static_cast<const uint8_t *>(codes);
+    p.scales = scales;
+    p.wcodes = static_cast<const uint8_t *>(w_dev);
+    p.wscales = reinterpret_cast<const uint16_t *>(p.wcodes + w->scales_offset);
+    p.rows = m;
+    p.n = w->n;
+    p.k = w->k;
+    p.experts = 1;
+    p.act_bits = act_bits;
+    p.y = y;
+    p.ldy = ldy;
+    return launch_status(bpg::launch_gemm(p, static_cast<hipStream_t>(stream)));
+}
+
+bpg_status w4a4_grouped_gemm(const void *codes, const float *scales, int act_bits,
+                             int64_t total_rows, const int32_t *expert_offsets_dev,
+                             const bpg_weights_desc *w, const void *w_dev, float *y,
+                             int64_t ldy, void *stream)
+{
+    if (!w)
+        return BPG_ERR_NULL;
+    bpg_status s = check_stamp(w);
+    if (s != BPG_OK)
+        return s;
+    s = check_act(codes, scales, act_bits, total_rows, w->k);
+    if (s != BPG_OK)
+        return s;
+    if (ldy < w->n)
+        return BPG_ERR_SHAPE;
+    if (!w_dev || !y || !expert_offsets_dev)
+        return BPG_ERR_NULL;
+    if (!aligned16(w_dev) || !aligned16(y) || ldy % 4 != 0 ||
+        (reinterpret_cast<uintptr_t>(expert_offsets_dev) & 3u) != 0)
+        return BPG_ERR_ALIGN;
+    s = check_device();
+    if (s != BPG_OK)
+        return s;
+    bpg::GemmProblem p{};
+    p.codes = static_cast<const uint8_t *>(codes);
+    p.scales = scales;
+    p.wcodes = static_cast<const uint8_t *>(w_dev);
+    p.wscales = reinterpret_cast<const uint16_t *>(p.wcodes + w->scales_offset);
+    p.rows = total_rows;
+    p.n = w->n;
+    p.k = w->k;
+    p.experts = w->num_experts;
+    p.act_bits = act_bits;
+    p.y = y;
+    p.ldy = ldy;
+    p.offsets = expert_offsets_dev;
+    return launch_status(bpg::launch_grouped_gemm(p, static_cast<hipStream_t>(stream)));
+}
+
+bpg_status w4a4_gemm_blocksums(const void *codes, const float *scales, int act_bits, int64_t m,
+                               const bpg_weights_desc *w, const void *w_dev, int64_t expert,
+                               int64_t m0, int64_t m1, int64_t n0, int64_t n1, int32_t *sums,
+                               void *stream)
+{
+    if (!w)
+        return BPG_ERR_NULL;
+    bpg_status s = check_stamp(w);
+    if (s != BPG_OK)
+        return s;
+    if (act_bits != 4 && act_bits != 8)
+        return BPG_ERR_DTYPE;
+    if (m < 0 || expert < 0 || expert >= w->num_experts || m0 < 0 || m0 > m1 || m1 > m ||
+        n0 < 0 || n0 > n1 || n1 > w->n || m > ((int64_t)1 << 31) - 1)
+        return BPG_ERR_SHAPE;
+    if (!codes || !w_dev || !sums)
+        return BPG_ERR_NULL;
+    if (!aligned16(codes) || !aligned16(w_dev) || !aligned16(sums) ||
+        (scales && !aligned16(scales)))
+        return BPG_ERR_ALIGN;
+    s = check_device();
+    if (s != BPG_OK)
+        return s;
+    bpg::GemmProblem p{};
+    p.codes = static_cast<const uint8_t *>(codes);
+    p.scales = scales;
+    p.wcodes = static_cast<const uint8_t *>(w_dev);
+    p.wscales = reinterpret_cast<const uint16_t *>(p.wcodes + w->scales_offset);
+    p.rows = m;
+    p.n = w->n;
+    p.k = w->k;
+    p.experts = w->num_experts;
+    p.act_bits = act_bits;
+    p.sums = sums;
+    p.m0 = m0;
+    p.m1 = m1;
+    p.n0 = n0;
+    p.n1 = n1;
+    p.expert = expert;
+    return launch_status(bpg::launch_blocksums(p, static_cast<hipStream_t>(stream)));
+}
+
+} // extern "C"

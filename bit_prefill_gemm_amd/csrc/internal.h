@@ -1,0 +1,37 @@
+// internal.h -- launchers shared between the C-ABI layer and the kernels.
+// Not part of the public interface (see include/bpg.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bpg {
+
+// Rotation + quantization of activations; dtype 0 = fp32, 1 = bf16 bits.
+hipError_t launch_quantize(const void *x, int dtype, int64_t m, int64_t k, int64_t ldx,
+                           int act_bits, int rotate, void *codes, float *scales,
+                           hipStream_t stream);
+
+// Arguments common to the dense, grouped and block-sum launches.
+struct GemmProblem {
+    const uint8_t *codes;    // activation codes, [rows][k/2] (4-bit) or [rows][k] (8-bit)
+    const float *scales;     // [rows][k/32]
+    const uint8_t *wcodes;   // image codes region
+    const uint16_t *wscales; // image scales region (fp16 bits)
+    int64_t rows;            // activation rows
+    int64_t n, k, experts;
+    int act_bits;
+    // dense / grouped output
+    float *y;
+    int64_t ldy;
+    const int32_t *offsets;  // grouped only: [experts+1] on the device
+    // block sums
+    int32_t *sums;
+    int64_t m0, m1, n0, n1, expert;
+};
+
+hipError_t launch_gemm(const GemmProblem &p, hipStream_t stream);
+hipError_t launch_grouped_gemm(const GemmProblem &p, hipStream_t stream);
+hipError_t launch_blocksums(const GemmProblem &p, hipStream_t stream);
+
+} // namespace bpg

@@ -1,0 +1,192 @@
+// quantize.hip -- FWHT-32 fused into per-block activation quantization (gfx950).
+//
+// "509 tokens a second of prompt: the Hadamard route ships", section "The
+// rotation": each 32-value block of activations is rotated by a 32-point
+// Walsh-Hadamard transform inside the quantize step, then rounded to 4-bit
+// codes sharing one scale.  The pages' RDNA design (two in-thread butterfly
+// steps plus three lane shuffles, wave32) is prior art; on CDNA4 (wave64) one
+// quad of lanes owns a block:
+//
+//   lane t of the quad holds elements {4t..4t+3} and {16+4t..16+4t+3};
+//   stage h=1 and h=2 pair elements inside each group of four (in-thread),
+//   stage h=4 pairs lane t with t^1 and h=8 pairs t with t^2 (DPP quad_perm),
+//   stage h=16 pairs element i with i+16 (in-thread, same lane).
+// The stage order is 1,2,4,8,16 and every stage gives the lower index a+b and
+// the upper a-b, each one fp32 rounding; then every value is multiplied by
+// fp32(1/sqrt(32)).  The block scale is amax/7 (8-bit route: amax/127) by
+// IEEE division and the code is rint(v/d) with ties to even, clamped.
+//
+// This file must be compiled with -ffp-contract=off: no operation above may be
+// fused into an FMA, so that the codes are bit-identical to a plain
+// step-by-step evaluation.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "internal.h"
+
+namespace bpg {
+
+namespace {
+
+constexpr int kThreads = 256;           // 64 blocks of 32 values per workgroup
+constexpr int kQuadXor1 = 0xB1;         // DPP quad_perm [1,0,3,2]
+constexpr int kQuadXor2 = 0x4E;         // DPP quad_perm [2,3,0,1]
+
+template <int CTRL>
+__device__ __forceinline__ float quad_swap(float v)
+{
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+
+// One butterfly stage across lanes: the lane whose `upper` flag is set holds
+// the upper element b and gets partner - own = a - b; the lower lane gets
+// own + partner = a + b.  Negation by flipping the sign bit is exact, so
+// partner + (-own) is the IEEE a - b.
+template <int CTRL>
+__device__ __forceinline__ void cross_stage(float (&v)[8], bool upper)
+{
+    const uint32_t flip = upper ? 0x80000000u : 0u;
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+        float p = quad_swap<CTRL>(v[i]);
+        v[i] = p + __uint_as_float(__float_as_uint(v[i]) ^ flip);
+    }
+}
+
+__device__ __forceinline__ void load8(const float *src, int t, float (&v)[8])
+{
+    float4 lo = *reinterpret_cast<const float4 *>(src + 4 * t);
+    float4 hi = *reinterpret_cast<const float4 *>(src + 16 + 4 * t);
+    v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
+    v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
+__device__ __forceinline__ void load8(const uint16_t *src, int t, float (&v)[8])
+{
+    uint2 lo = *reinterpret_cast<const uint2 *>(src + 4 * t);
+    uint2 hi = *reinterpret_cast<const uint2 *>(src + 16 + 4 * t);
+    v[0] = bf16_to_f32(lo.x & 0xFFFFu); v[1] = bf16_to_f32(lo.x >> 16);
+    v[2] = bf16_to_f32(lo.y & 0xFFFFu); v[3] = bf16_to_f32(lo.y >> 16);
+    v[4] = bf16_to_f32(hi.x & 0xFFFFu); v[5] = bf16_to_f32(hi.x >> 16);
+    v[6] = bf16_to_f32(hi.y & 0xFFFFu); v[7] = bf16_to_f32(hi.y >> 16);
+}
+
+template <typename T, int BITS>
+__global__ __launch_bounds__(kThreads) void quantize_h32_kernel(
+    const T *__restrict__ x, int64_t k, int64_t ldx, int64_t nblk_total, int rotate,
+    uint8_t *__restrict__ codes, float *__restrict__ scales)
+{
+    const int64_t blk = (int64_t)blockIdx.x * (kThreads / 4) + (threadIdx.x >> 2);
+    const int t = threadIdx.x & 3;
+    // All four lanes of a quad share `blk`, so a quad exits as a whole and the
+    // quad-local DPP exchanges below never read an exited lane.
+    if (blk >= nblk_total)
+        return;
+    const int64_t nb = k / 32;
+    const int64_t row = blk / nb;
+    const int64_t b = blk - row * nb;
+
+    float v[8];
+    load8(x + row * ldx + b * 32, t, v);
+
+    if (rotate) {
+        // h = 1: pairs (4t, 4t+1), (4t+2, 4t+3) and the same in the upper half
+#pragma unroll
+        for (int base = 0; base < 8; base += 4) {
+            float a0 = v[base], a1 = v[base + 1], a2 = v[base + 2], a3 = v[base + 3];
+            v[base] = a0 + a1; v[base + 1] = a0 - a1;
+            v[base + 2] = a2 + a3; v[base + 3] = a2 - a3;
+        }
+        // h = 2: pairs (4t, 4t+2), (4t+1, 4t+3)
+#pragma unroll
+        for (int base = 0; base < 8; base += 4) {
+            float a0 = v[base], a1 = v[base + 1], a2 = v[base + 2], a3 = v[base + 3];
+            v[base] = a0 + a2; v[base + 2] = a0 - a2;
+            v[base + 1] = a1 + a3; v[base + 3] = a1 - a3;
+        }
+        // h = 4: element 4t+i pairs with 4(t^1)+i; the even lane is lower
+        cross_stage<kQuadXor1>(v, (t & 1) != 0);
+        // h = 8: lane t pairs with t^2; lanes 0,1 are lower
+        cross_stage<kQuadXor2>(v, (t & 2) != 0);
+        // h = 16: element j (v[i]) pairs with j+16 (v[i+4]) in the same lane
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            float a = v[i], c = v[i + 4];
+            v[i] = a + c;
+            v[i + 4] = a - c;
+        }
+        const float inv_sqrt32 = __uint_as_float(0x3E3504F3u); // fp32 nearest to 1/sqrt(32)
+#pragma unroll
+        for (int i = 0; i < 8; i++)
+            v[i] = v[i] * inv_sqrt32;
+    }
+
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; i++)
+        amax = fmaxf(amax, fabsf(v[i]));
+    amax = fmaxf(amax, quad_swap<kQuadXor1>(amax));
+    amax = fmaxf(amax, quad_swap<kQuadXor2>(amax));
+
+    constexpr float kQmax = BITS == 4 ? 7.0f : 127.0f;
+    constexpr float kQmin = BITS == 4 ? -8.0f : -127.0f;
+    const float d = amax == 0.0f ? 0.0f : amax / kQmax;
+    int q[8];
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+        float r = amax == 0.0f ? 0.0f : rintf(v[i] / d);
+        r = fminf(fmaxf(r, kQmin), kQmax);
+        q[i] = (int)r;
+    }
+
+    if (BITS == 4) {
+        // byte 4t+i = code(4t+i) low nibble | code(16+4t+i) high nibble
+        uint32_t word = 0;
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+            word |= (uint32_t)((q[i] & 0xF) | ((q[i + 4] & 0xF) << 4)) << (8 * i);
+        *reinterpret_cast<uint32_t *>(codes + row * (k / 2) + b * 16 + 4 * t) = word;
+    } else {
+        uint32_t lo = 0, hi = 0;
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            lo |= (uint32_t)(q[i] & 0xFF) << (8 * i);
+            hi |= (uint32_t)(q[i + 4] & 0xFF) << (8 * i);
+        }
+        uint8_t *dst = codes + row * k + b * 32;
+        *reinterpret_cast<uint32_t *>(dst + 4 * t) = lo;
+        *reinterpret_cast<uint32_t *>(dst + 16 + 4 * t) = hi;
+    }
+    if (t == 0)
+        scales[row * nb + b] = d;
+}
+
+} // namespace
+
+hipError_t launch_quantize(const void *x, int dtype, int64_t m, int64_t k, int64_t ldx,
+                           int act_bits, int rotate, void *codes, float *scales,
+                           hipStream_t stream)
+{
+    const int64_t nblk = m * (k / 32);
+    if (nblk == 0)
+        return hipSuccess;
+    const dim3 grid((unsigned)((nblk + kThreads / 4 - 1) / (kThreads / 4)));
+    uint8_t *c = static_cast<uint8_t *>(codes);
+    if (dtype == 0 && act_bits == 4)
+        quantize_h32_kernel<float, 4><<<grid, kThreads, 0, stream>>>(
+            static_cast<const float *>(x), k, ldx, nblk, rotate, c, scales);
+    else if (dtype == 0)
+        quantize_h32_kernel<float, 8><<<grid, kThreads, 0, stream>>>(
+            static_cast<const float *>(x), k, ldx, nblk, rotate, c, scales);
+    else if (act_bits == 4)
+        quantize_h32_kernel<uint16_t, 4><<<grid, kThreads, 0, stream>>>(
+            static_cast<const uint16_t *>(x), k, ldx, nblk, rotate, c, scales);
+    else
+        quantize_h32_kernel<uint16_t, 8><<<grid, kThreads, 0, stream>>>(
+            static_cast<const uint16_t *>(x), k, ldx, nblk, rotate, c, scales);
+    return hipGetLastError();
+}
+
+} // namespace bpg

@@ -1,0 +1,207 @@
+/*
+ * bpg.h -- C ABI of the MI355X (gfx950) Hadamard-rotated W4A4 prompt GEMM.
+ *
+ * The method ("509 tokens a second of prompt: the Hadamard route ships",
+ * sections "Why prompts are a matrix-unit problem" and "The rotation"; and
+ * "Qwen3.8-27B at 45.7 tok/s: DFlash2 in 1bit serve, and 4-bit activations
+ * with a Hadamard rotation", section "Prompt processing: 4-bit activations,
+ * rotated first"):
+ *   - every 32-value block of the activations is rotated by a 32-point
+ *     Walsh-Hadamard transform and rounded to 4-bit codes sharing one scale;
+ *   - the weights are Q4_0 (4-bit code u meaning u-8, one fp16 scale per 32)
+ *     that were rotated the same way once, offline, so x.w = (Hx).(Hw);
+ *   - the product runs on integer matrix instructions; the kernel reads the
+ *     Q4_0 nibbles bit for bit, flipping each code's top bit to get u-8 in
+ *     two's complement.
+ * The MoE variant ("Where the engine is going: HRX and the NPU", section
+ * "4-bit activations reach the MoE experts") runs the same route over the
+ * expert matmuls.  The 8-bit activation route is the pages' "exact 8-bit"
+ * comparison path.
+ *
+ * Numerics fixed by this library (the pages are silent on them):
+ *   - rotation: Sylvester-order H32, butterfly stages h = 1,2,4,8,16 in fp32
+ *     (lower index a+b, upper a-b), then times fp32(1/sqrt(32)); no FMA;
+ *   - scale d = amax/7 (8-bit: amax/127), IEEE fp32 division; code
+ *     q = clamp(rint(v/d), -8, 7) (8-bit: +-127), ties to even; all-zero block:
+ *     d = 0, codes 0;
+ *   - block dot products are exact int32; the output is
+ *     y[m][n] = sum_b da[m][b] * dw[n][b] * S[m][n][b], accumulated in fp32
+ *     in a fixed order per shape (bit-identical from run to run).
+ *
+ * Conventions for every call:
+ *   - returns bpg_status; BPG_OK on success.  No call allocates device memory,
+ *     keeps a pointer after returning, or logs;
+ *   - all argument and stamp checks run on the host, before any HIP call, so
+ *     every error except BPG_ERR_DEVICE / BPG_ERR_LAUNCH is reported without
+ *     touching a GPU;
+ *   - device calls are asynchronous on `stream` (a hipStream_t; NULL = the
+ *     null stream); execution faults surface at the caller's synchronisation;
+ *   - the caller owns every buffer; device pointers must be 16-byte aligned;
+ *   - K (input channels) is a multiple of 32, N (output channels) a multiple
+ *     of 32; M (tokens) may be 0 (the call is then a no-op after its checks);
+ *   - inputs are finite; NaN or Inf input gives unspecified codes.
+ */
+#ifndef BPG_H
+#define BPG_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    BPG_OK = 0,
+    BPG_ERR_NULL = 1,   /* a required pointer is NULL */
+    BPG_ERR_SHAPE = 2,  /* a size is negative, K or N not a multiple of 32, ld too small, ... */
+    BPG_ERR_ALIGN = 3,  /* a device pointer or leading dimension breaks the alignment rule */
+    BPG_ERR_DTYPE = 4,  /* unknown dtype or source kind, or act_bits not 4 or 8 */
+    BPG_ERR_STAMP = 5,  /* weight descriptor not made by rotate_pack_weights, wrong
+                           version or layout, not rotated, or sizes that disagree */
+    BPG_ERR_BUFFER = 6, /* destination buffer too small */
+    BPG_ERR_DEVICE = 7, /* the current device is not a gfx950 GPU */
+    BPG_ERR_LAUNCH = 8  /* the kernel launch failed (hipGetLastError after enqueue) */
+} bpg_status;
+
+/* Source of rotate_pack_weights. */
+typedef enum {
+    BPG_SRC_F32 = 0,           /* unrotated float weights [E][N][K], fp32 */
+    BPG_SRC_BF16 = 1,          /* unrotated float weights [E][N][K], bf16 bits */
+    BPG_SRC_Q4_0_ROTATED = 2   /* Q4_0 blocks [E][N][K/32] x 18 B of weights already
+                                  rotated by H32 (a rotated file's tensors) */
+} bpg_src_kind;
+
+/* Activation dtype of quantize_act_h32. */
+typedef enum { BPG_X_F32 = 0, BPG_X_BF16 = 1 } bpg_x_dtype;
+
+#define BPG_WEIGHTS_MAGIC 0x57475042u /* "BPGW" little-endian */
+#define BPG_WEIGHTS_VERSION 1u
+#define BPG_LAYOUT_COLTILE32 1u
+
+/*
+ * Stamp of a packed weight image (the analogue of the rotated file's stamp:
+ * a GEMM refuses an image whose stamp is missing or does not say rotated).
+ *
+ * Device image, layout BPG_LAYOUT_COLTILE32, for E experts (1 if dense),
+ * B = K/32 blocks per row and N/32 column tiles:
+ *   codes  at byte 0:           [E][N/32][B][32 columns][16 B]   the 16 Q4_0
+ *          nibble bytes of block (n, b) verbatim (byte j: element j in the low
+ *          nibble, element j+16 in the high nibble; code u means u-8);
+ *   scales at scales_offset:    [E][N/32][B][32 columns] fp16, the block scale.
+ * Total bytes = E*N*K*18/32, as for Q4_0.
+ */
+typedef struct {
+    uint32_t magic;        /* BPG_WEIGHTS_MAGIC */
+    uint32_t version;      /* BPG_WEIGHTS_VERSION */
+    uint32_t rotation;     /* 32: every block rotated by H32 */
+    uint32_t layout;       /* BPG_LAYOUT_COLTILE32 */
+    int64_t n;             /* output channels per expert */
+    int64_t k;             /* input channels */
+    int64_t num_experts;   /* 1 for a dense weight */
+    uint64_t bytes;        /* size of the image */
+    uint64_t scales_offset;/* byte offset of the scales region */
+} bpg_weights_desc;
+
+/* Human-readable name of a status (static string). */
+const char *bpg_status_str(bpg_status s);
+
+/* Size in bytes of the packed image for the given shape; 0 if the shape is invalid. */
+size_t rotate_pack_weights_bytes(int64_t n, int64_t k, int64_t num_experts);
+
+/*
+ * Offline weight preparation, on the CPU, synchronous
+ * ("509 tokens a second of prompt: the Hadamard route ships", section
+ * "Making the file is part of the engine": the tool rotates the projections,
+ * quantizes to Q4_0 and stamps the file).
+ *
+ *   src       host pointer; layout given by `kind` (see bpg_src_kind)
+ *   n, k      per-expert output and input channels (both multiples of 32)
+ *   num_experts  >= 1
+ *   dst_host  host buffer of at least rotate_pack_weights_bytes(n, k, E) bytes;
+ *             receives the device image, to be copied to the GPU as-is
+ *   desc_out  receives the stamp
+ *
+ * Float sources are rotated per 32-block in fp64 (same butterfly order, times
+ * fp64 1/sqrt(32)) and quantized to Q4_0: dw = fp16(amax/7), u = clamp(
+ * rint(w'/dw), -8, 7) + 8 with the fp16-rounded dw.  Q4_0 sources are only
+ * re-laid out.  Errors: NULL, SHAPE, DTYPE, BUFFER.
+ */
+bpg_status rotate_pack_weights(const void *src, bpg_src_kind kind, int64_t n, int64_t k,
+                               int64_t num_experts, void *dst_host, size_t dst_bytes,
+                               bpg_weights_desc *desc_out);
+
+/*
+ * FWHT-32 fused into per-block activation quantization, on the GPU
+ * ("509 tokens a second of prompt: the Hadamard route ships", section
+ * "The rotation": the rotation runs inside the step that quantizes
+ * activations; blocks of 32 values share one scale).
+ *
+ *   x        device, [m][ldx] elements of `dt` (fp32, or bf16 bits); ldx >= k,
+ *            ldx % 4 == 0
+ *   act_bits 4: codes [m][k/2] bytes, each block's 16 bytes holding element j
+ *            in the low nibble and element j+16 in the high nibble of byte j
+ *            (4-bit two's complement, the Q4_0 pairing);
+ *            8: codes [m][k] int8 in natural element order
+ *   scales   device, [m][k/32] fp32
+ * Errors: NULL, SHAPE, ALIGN, DTYPE, DEVICE, LAUNCH.
+ */
+bpg_status quantize_act_h32(const void *x, bpg_x_dtype dt, int64_t m, int64_t k, int64_t ldx,
+                            int act_bits, void *codes, float *scales, void *stream);
+
+/*
+ * Dense W4A4 (or W4A8) product y = x . W^T from codes, on the GPU
+ * ("509 tokens a second of prompt: the Hadamard route ships", section
+ * "Why prompts are a matrix-unit problem").
+ *
+ *   codes, scales  device, as written by quantize_act_h32 for m rows and k = w->k
+ *   act_bits       4 or 8, as given to quantize_act_h32
+ *   w, w_dev       stamp (host) and device copy of the image; w->num_experts == 1
+ *   y              device, [m][ldy] fp32, ldy >= w->n, ldy % 4 == 0; overwritten
+ * Errors: NULL, SHAPE, ALIGN, DTYPE, STAMP, DEVICE, LAUNCH.
+ */
+bpg_status w4a4_gemm(const void *codes, const float *scales, int act_bits, int64_t m,
+                     const bpg_weights_desc *w, const void *w_dev, float *y, int64_t ldy,
+                     void *stream);
+
+/*
+ * Grouped (MoE) product over ragged expert row ranges, on the GPU
+ * ("Where the engine is going: HRX and the NPU", section "4-bit activations
+ * reach the MoE experts").  Rows of `codes` are sorted by expert: expert e
+ * owns rows [offsets[e], offsets[e+1]) and multiplies them by its weights.
+ *
+ *   total_rows          rows of codes/scales/y
+ *   expert_offsets_dev  device, int32 [E+1], non-decreasing, offsets[0] >= 0,
+ *                       offsets[E] <= total_rows, E = w->num_experts.  Not
+ *                       read on the host (no synchronisation).  Values that
+ *                       break the rule give unspecified rows of y, but every
+ *                       access stays inside [0, total_rows).
+ *   y                   device, [total_rows][ldy] fp32; rows outside every
+ *                       expert's range are left untouched
+ * Errors: NULL, SHAPE, ALIGN, DTYPE, STAMP, DEVICE, LAUNCH.
+ */
+bpg_status w4a4_grouped_gemm(const void *codes, const float *scales, int act_bits,
+                             int64_t total_rows, const int32_t *expert_offsets_dev,
+                             const bpg_weights_desc *w, const void *w_dev, float *y,
+                             int64_t ldy, void *stream);
+
+/*
+ * Parity and debug: the exact int32 block dot products
+ * S[m][n][b] = sum_i q_a[m][32b+i] * (u[n][32b+i] - 8), computed by the same
+ * matrix-instruction main loop as w4a4_gemm, for rows [m0, m1) and columns
+ * [n0, n1) of expert `expert` (0 for a dense image).
+ *
+ *   scales  not read (may be NULL)
+ *   sums    device, int32 [(m1-m0)][(n1-n0)][k/32]
+ * Errors: NULL, SHAPE, ALIGN, DTYPE, STAMP, DEVICE, LAUNCH.
+ */
+bpg_status w4a4_gemm_blocksums(const void *codes, const float *scales, int act_bits, int64_t m,
+                               const bpg_weights_desc *w, const void *w_dev, int64_t expert,
+                               int64_t m0, int64_t m1, int64_t n0, int64_t n1, int32_t *sums,
+                               void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BPG_H */

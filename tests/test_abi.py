@@ -1,0 +1,168 @@
+"""The C ABI: the library loads without a GPU, exports every declared entry
+point, and reports every argument and stamp error from the host, before any
+HIP call.  Pointers used here are never dereferenced: each call fails its
+checks first (or, for the last test, at the device check on a GPU-less host).
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from bit_prefill_gemm_amd import binding as bb
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bpg.h")
+
+OK, NULL, SHAPE, ALIGN, DTYPE, STAMP, BUFFER, DEVICE = 0, 1, 2, 3, 4, 5, 6, 7
+
+P = ctypes.c_void_p(0x100000)        # aligned, never dereferenced
+P2 = ctypes.c_void_p(0x200000)
+MIS = ctypes.c_void_p(0x100004)      # 4-byte aligned only
+NUL = ctypes.c_void_p(0)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^[A-Za-z_][\w \*]*?\b([a-z_][a-z0-9_]*)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_library_exports_every_declared_function():
+    lib = bb.lib()
+    names = declared_functions()
+    assert set(names) == set(bb.ENTRY_POINTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    lib = bb.lib()
+    for s in range(9):
+        assert lib.bpg_status_str(s)
+    assert b"unknown" in lib.bpg_status_str(99)
+
+
+def good_desc(n=64, k=128, e=1):
+    d = bb.WeightsDesc()
+    d.magic, d.version, d.rotation, d.layout = 0x57475042, 1, 32, 1
+    d.n, d.k, d.num_experts = n, k, e
+    d.bytes = e * n * (k // 32) * 18
+    d.scales_offset = e * n * (k // 32) * 16
+    return d
+
+
+def q(x=P, dt=0, m=4, k=128, ldx=128, bits=4, codes=P2, scales=P, stream=NUL):
+    return bb.lib().quantize_act_h32(x, dt, m, k, ldx, bits, codes, scales, stream)
+
+
+def gemm(codes=P, scales=P2, bits=4, m=4, desc=None, wdev=P, y=P2, ldy=64, stream=NUL):
+    d = desc if desc is not None else good_desc()
+    return bb.lib().w4a4_gemm(codes, scales, bits, m, ctypes.byref(d), wdev, y, ldy, stream)
+
+
+def grouped(codes=P, scales=P2, bits=4, rows=4, off=P, desc=None, wdev=P, y=P2, ldy=64,
+            stream=NUL):
+    d = desc if desc is not None else good_desc(e=3)
+    return bb.lib().w4a4_grouped_gemm(codes, scales, bits, rows, off, ctypes.byref(d), wdev, y,
+                                      ldy, stream)
+
+
+def sums(codes=P, scales=P2, bits=4, m=4, desc=None, wdev=P, expert=0, m0=0, m1=4, n0=0,
+         n1=64, out=P2, stream=NUL):
+    d = desc if desc is not None else good_desc()
+    return bb.lib().w4a4_gemm_blocksums(codes, scales, bits, m, ctypes.byref(d), wdev, expert,
+                                        m0, m1, n0, n1, out, stream)
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(dt=2), DTYPE), (dict(bits=3), DTYPE), (dict(bits=16), DTYPE),
+    (dict(k=100, ldx=100), SHAPE), (dict(k=0, ldx=0), SHAPE), (dict(m=-1), SHAPE),
+    (dict(ldx=96), SHAPE),
+    (dict(x=NUL), NULL), (dict(codes=NUL), NULL), (dict(scales=NUL), NULL),
+    (dict(x=MIS), ALIGN), (dict(codes=MIS), ALIGN), (dict(ldx=130), ALIGN),
+])
+def test_quantize_errors(kwargs, status):
+    assert q(**kwargs) == status
+
+
+def _desc_with(**kw):
+    d = good_desc()
+    for a, v in kw.items():
+        setattr(d, a, v)
+    return d
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(desc=_desc_with(magic=0)), STAMP),
+    (dict(desc=_desc_with(version=2)), STAMP),
+    (dict(desc=_desc_with(rotation=0)), STAMP),      # an unrotated image is refused
+    (dict(desc=_desc_with(rotation=64)), STAMP),
+    (dict(desc=_desc_with(layout=0)), STAMP),
+    (dict(desc=_desc_with(bytes=1)), STAMP),
+    (dict(desc=_desc_with(scales_offset=8)), STAMP),
+    (dict(desc=_desc_with(n=48)), STAMP),
+    (dict(desc=good_desc(e=2)), STAMP),              # dense call on an expert image
+    (dict(bits=2), DTYPE), (dict(m=-3), SHAPE), (dict(ldy=32), SHAPE),
+    (dict(codes=NUL), NULL), (dict(scales=NUL), NULL), (dict(wdev=NUL), NULL),
+    (dict(y=NUL), NULL), (dict(y=MIS), ALIGN), (dict(codes=MIS), ALIGN), (dict(ldy=66), ALIGN),
+])
+def test_gemm_errors(kwargs, status):
+    assert gemm(**kwargs) == status
+
+
+def test_gemm_null_desc():
+    lib = bb.lib()
+    assert lib.w4a4_gemm(P, P2, 4, 4, None, P, P2, 64, NUL) == NULL
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(off=NUL), NULL), (dict(off=ctypes.c_void_p(0x100002)), ALIGN),
+    (dict(bits=7), DTYPE), (dict(rows=-1), SHAPE),
+    (dict(desc=_desc_with(magic=1)), STAMP),
+])
+def test_grouped_errors(kwargs, status):
+    assert grouped(**kwargs) == status
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(m0=3, m1=2), SHAPE), (dict(m1=5), SHAPE), (dict(n1=65), SHAPE), (dict(n0=-1), SHAPE),
+    (dict(expert=1), SHAPE), (dict(expert=-1), SHAPE), (dict(out=NUL), NULL),
+    (dict(bits=1), DTYPE), (dict(out=MIS), ALIGN), (dict(desc=_desc_with(rotation=16)), STAMP),
+])
+def test_blocksum_errors(kwargs, status):
+    assert sums(**kwargs) == status
+
+
+def test_pack_errors():
+    lib = bb.lib()
+    d = bb.WeightsDesc()
+    src = np.zeros(64 * 4 * 18, dtype=np.uint8)
+    dst = np.zeros(64 * 4 * 18, dtype=np.uint8)
+    sp, dp = src.ctypes.data_as(ctypes.c_void_p), dst.ctypes.data_as(ctypes.c_void_p)
+    assert lib.rotate_pack_weights(sp, 9, 64, 128, 1, dp, dst.nbytes, ctypes.byref(d)) == DTYPE
+    assert lib.rotate_pack_weights(sp, 2, 48, 128, 1, dp, dst.nbytes, ctypes.byref(d)) == SHAPE
+    assert lib.rotate_pack_weights(sp, 2, 64, 100, 1, dp, dst.nbytes, ctypes.byref(d)) == SHAPE
+    assert lib.rotate_pack_weights(sp, 2, 64, 128, 0, dp, dst.nbytes, ctypes.byref(d)) == SHAPE
+    assert lib.rotate_pack_weights(NUL, 2, 64, 128, 1, dp, dst.nbytes, ctypes.byref(d)) == NULL
+    assert lib.rotate_pack_weights(sp, 2, 64, 128, 1, dp, dst.nbytes - 1, ctypes.byref(d)) == BUFFER
+    assert lib.rotate_pack_weights(sp, 2, 64, 128, 1, dp, dst.nbytes, ctypes.byref(d)) == OK
+    assert lib.rotate_pack_weights_bytes(64, 128, 1) == 64 * 4 * 18
+    assert lib.rotate_pack_weights_bytes(63, 128, 1) == 0
+    assert lib.rotate_pack_weights_bytes(64, 128, -1) == 0
+
+
+@pytest.mark.skipif(os.path.exists("/dev/kfd"), reason="host has a GPU driver")
+def test_valid_calls_stop_at_device_check_without_gpu():
+    assert q() == DEVICE
+    assert gemm() == DEVICE
+    assert grouped() == DEVICE
+    assert sums() == DEVICE
+
+
+def test_binding_raises_typed_error():
+    with pytest.raises(bb.BpgError) as ei:
+        bb.rotate_pack_weights(np.zeros(10, dtype=np.uint8), 7, 64, 128)
+    assert ei.value.status == DTYPE

@@ -1,0 +1,305 @@
+"""GPU parity: the HIP path, called through the C ABI, against the CPU oracle.
+
+Bar: activation codes, scales and int32 block sums bit-exact; fp32 outputs
+within 1e-3 of the oracle's fp64 output in row-L2 relative error (and, as a
+tighter regression check, within the fp32 accumulation error).
+"""
+import numpy as np
+import pytest
+
+import oracle
+from bit_prefill_gemm_amd import binding as bb
+from bit_prefill_gemm_amd import synth
+
+from gpu_util import (act_to_device, oracle_codes, rects, row_rel_err, sample_rows,
+                      torch_mod, weights_to_device)
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-3        # row-L2 relative error, the contract
+TIGHT = 2e-5      # fp32 accumulation over up to 544 blocks sits far below this
+
+
+@pytest.fixture(scope="module")
+def torch():
+    t = torch_mod()
+    if not t.cuda.is_available():
+        pytest.skip("no GPU")
+    return t
+
+
+def quantize_and_check(x, bits, rotate_ref=True):
+    """Quantize on the GPU, compare codes and scales bit-exactly, return device + oracle codes."""
+    torch = torch_mod()
+    xd = act_to_device(x)
+    codes, scales = bb.quantize_act_h32(xd, bits)
+    torch.cuda.synchronize()
+    q, d, _ = oracle.quantize(x, bits)
+    got_codes = codes.cpu().numpy()
+    got_scales = scales.cpu().numpy()
+    exp_codes = oracle_codes(q, bits)
+    bad = np.argwhere(got_codes != exp_codes)
+    assert bad.size == 0, "codes differ at %s (of %d)" % (bad[:5].tolist(), len(bad))
+    assert np.array_equal(got_scales.view(np.uint32), d.view(np.uint32)), "scales differ"
+    return codes, scales, q, d
+
+
+# ------------------------------------------------------------------ quantizer
+
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("name,key", [("tiny", "x"), ("attn512", "x"), ("long1024", "x"),
+                                      ("ffn512", "x1"), ("ffn512", "x2"), ("moe512", "x_gu"),
+                                      ("moe512", "x_dn"), ("m16_down", "x")])
+def test_quantize_parity_workloads(torch, name, key, bits):
+    print("quantize", name, key, bits, flush=True)
+    quantize_and_check(synth.make(name)[key], bits)
+
+
+def test_quantize_edge_cases(torch):
+    rng = np.random.default_rng(31)
+    x = rng.standard_normal((7, 96)).astype(np.float32)
+    x[0] = 0.0                                   # all-zero row
+    x[1, :32] = 2.5                              # constant block
+    x[2, 32:64] = 1e-30                          # tiny block
+    x[3, 64:96] = 1e30                           # huge block
+    x[4, 5] = -40.0                              # spike
+    x[5, :32] = 0.0
+    x[5, 17] = 1e-3                              # one nonzero
+    for bits in (4, 8):
+        quantize_and_check(x, bits)
+        quantize_and_check(x[:1], bits)          # M = 1
+        quantize_and_check(np.ascontiguousarray(x[:, :32]), bits)   # K = 32
+
+
+def test_quantize_strided_rows(torch):
+    """ldx > k: quantize the left half of a wider matrix."""
+    rng = np.random.default_rng(32)
+    full = synth.bf16_bits(rng.standard_normal((33, 256)).astype(np.float32))
+    xd = act_to_device(full)[:, :160]
+    assert xd.stride(0) == 256
+    codes, scales = bb.quantize_act_h32(xd, 4)
+    q, d, _ = oracle.quantize(np.ascontiguousarray(full[:, :160]), 4)
+    assert np.array_equal(codes.cpu().numpy(), oracle.pack_int4(q))
+    assert np.array_equal(scales.cpu().numpy().view(np.uint32), d.view(np.uint32))
+
+
+def test_quantize_empty(torch):
+    x = torch.empty((0, 64), dtype=torch.float32, device="cuda")
+    codes, scales = bb.quantize_act_h32(x, 4)
+    assert codes.shape == (0, 32) and scales.shape == (0, 2)
+
+
+# ------------------------------------------------------------------ block sums
+
+def check_blocksums(codes, scales, bits, W, q, w, rect_list, expert=0):
+    torch = torch_mod()
+    for (m0, m1, n0, n1) in rect_list:
+        print("blocksums", bits, (m0, m1, n0, n1), "expert", expert, flush=True)
+        s = bb.w4a4_gemm_blocksums(codes, scales, bits, W, m0, m1, n0, n1, expert=expert)
+        torch.cuda.synchronize()
+        ref = oracle.block_sums(q, w, m0, m1, n0, n1)
+        got = s.cpu().numpy()
+        bad = np.argwhere(got != ref)
+        assert bad.size == 0, "block sums differ at %s" % bad[:5].tolist()
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_blocksums_tiny_full(torch, bits):
+    t = synth.make("tiny")
+    codes, scales, q, _ = quantize_and_check(t["x"], bits)
+    W = weights_to_device(t["w"], 128, 256)
+    w, _ = oracle.q4_0_decode(t["w"], 256)
+    check_blocksums(codes, scales, bits, W, q, w, [(0, 16, 0, 128), (3, 11, 17, 90)])
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_blocksums_attn512_sampled(torch, bits):
+    t = synth.make("attn512")
+    codes, scales, q, _ = quantize_and_check(t["x"], bits)
+    W = weights_to_device(t["w"], 5120, 5120)
+    w, _ = oracle.q4_0_decode(t["w"], 5120)
+    check_blocksums(codes, scales, bits, W, q, w, rects(512, 5120, 64, 3, seed=bits))
+
+
+def test_blocksums_ffn_down_sampled(torch):
+    t = synth.make("ffn512")
+    codes, scales, q, _ = quantize_and_check(t["x2"], 4)
+    W = weights_to_device(t["w_down"], 5120, 17408)
+    w, _ = oracle.q4_0_decode(t["w_down"], 17408)
+    check_blocksums(codes, scales, 4, W, q, w, rects(512, 5120, 64, 2, seed=5))
+
+
+# ------------------------------------------------------------------ dense GEMM
+
+def check_gemm(x, blocks, n, k, bits, rows=None, label=""):
+    torch = torch_mod()
+    codes, scales, q, d = quantize_and_check(x, bits)
+    W = weights_to_device(blocks, n, k)
+    print("gemm", label, x.shape, n, bits, flush=True)
+    y = bb.w4a4_gemm(codes, scales, bits, W)
+    torch.cuda.synchronize()
+    w, dw = oracle.q4_0_decode(blocks, k)
+    m = x.shape[0]
+    rows = np.arange(m) if rows is None else rows
+    yg = y.cpu().numpy()[rows]
+    ref = np.concatenate([oracle.gemm_rect(q, d, w, dw, r, r + 1, 0, n) for r in rows])
+    err = row_rel_err(yg, ref)
+    assert err <= TOL, err
+    assert err <= TIGHT, err
+    return y, err
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_gemm_tiny_full(torch, bits):
+    t = synth.make("tiny")
+    check_gemm(t["x"], t["w"], 128, 256, bits, label="tiny")
+
+
+@pytest.mark.parametrize("m,k,n", [(100, 320, 96), (1, 64, 32), (16, 256, 128), (33, 128, 64),
+                                   (64, 32, 160), (130, 96, 224), (257, 1056, 64)])
+@pytest.mark.parametrize("bits", [4, 8])
+def test_gemm_ragged_shapes(torch, m, k, n, bits):
+    case = synth.small_dense(m, k, n, seed=m + k + n)
+    check_gemm(case["x"], case["w"], n, k, bits, label="ragged")
+
+
+def test_gemm_m0_is_noop(torch):
+    case = synth.small_dense(4, 64, 32, seed=1)
+    W = weights_to_device(case["w"], 32, 64)
+    codes = torch.zeros((0, 32), dtype=torch.uint8, device="cuda")
+    scales = torch.zeros((0, 2), dtype=torch.float32, device="cuda")
+    y = torch.full((0, 32), 7.0, device="cuda")
+    bb.w4a4_gemm(codes, scales, 4, W, y=y)
+    torch.cuda.synchronize()
+
+
+def test_gemm_output_stride(torch):
+    case = synth.small_dense(40, 128, 64, seed=2)
+    codes, scales, q, d = quantize_and_check(case["x"], 4)
+    W = weights_to_device(case["w"], 64, 128)
+    ybig = torch.full((40, 100), -1.0, device="cuda")
+    y = ybig[:, 4:68]
+    assert y.stride(0) == 100
+    bb.w4a4_gemm(codes, scales, 4, W, y=y)
+    torch.cuda.synchronize()
+    yb = ybig.cpu().numpy()
+    assert np.all(yb[:, :4] == -1.0) and np.all(yb[:, 68:] == -1.0)
+    w, dw = oracle.q4_0_decode(case["w"], 128)
+    ref = oracle.gemm_rect(q, d, w, dw, 0, 40, 0, 64)
+    assert row_rel_err(yb[:, 4:68], ref) <= TIGHT
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_gemm_attn512_full_size(torch, bits):
+    """The benchmarked workload, in the benchmarked launch configuration."""
+    t = synth.make("attn512")
+    check_gemm(t["x"], t["w"], 5120, 5120, bits, rows=sample_rows(512, 24, seed=bits),
+               label="attn512")
+
+
+def test_gemm_ffn512_full_size(torch):
+    t = synth.make("ffn512")
+    rows = sample_rows(512, 8, seed=3)
+    check_gemm(t["x1"], t["w_gate"], 17408, 5120, 4, rows=rows, label="ffn gate")
+    check_gemm(t["x1"], t["w_up"], 17408, 5120, 4, rows=rows, label="ffn up")
+    check_gemm(t["x2"], t["w_down"], 5120, 17408, 4, rows=rows, label="ffn down")
+
+
+@pytest.mark.parametrize("name", ["m16_gate", "m16_down", "m16_attn"])
+def test_gemm_m16_full_size(torch, name):
+    t = synth.make(name)
+    c = t["cfg"]
+    check_gemm(t["x"], t["w"], c["n"], c["k"], 4, label=name)
+
+
+def test_long1024_routes_and_error_vs_unquantized(torch):
+    """Both routes match the oracle; report their error against the fp64 unquantized product."""
+    t = synth.make("long1024")
+    rows = sample_rows(1024, 6, seed=4)
+    cols = np.arange(17408)
+    w, dw = oracle.q4_0_decode(t["w"], 5120)
+    rr, cc = np.meshgrid(rows, cols, indexing="ij")
+    ref = oracle.ref_points(t["x"], w, dw, rr.ravel(), cc.ravel()).reshape(len(rows), -1)
+    errs = {}
+    for bits in (4, 8):
+        y, _ = check_gemm(t["x"], t["w"], 17408, 5120, bits, rows=rows, label="long1024")
+        errs[bits] = row_rel_err(y.cpu().numpy()[rows], ref)
+    print("error vs fp64 unquantized: int4 %.4g, q8 %.4g" % (errs[4], errs[8]))
+    assert errs[8] < errs[4] < 0.5
+
+
+# ------------------------------------------------------------------ grouped GEMM
+
+def check_grouped(x, blocks, offsets, n, k, E, bits, rows=None, label=""):
+    torch = torch_mod()
+    codes, scales, q, d = quantize_and_check(x, bits)
+    W = weights_to_device(blocks, n, k, E)
+    off = torch.from_numpy(offsets.astype(np.int32)).cuda()
+    total = x.shape[0]
+    print("grouped", label, total, n, k, E, bits, flush=True)
+    y = torch.full((total, n), float("nan"), device="cuda")
+    bb.w4a4_grouped_gemm(codes, scales, bits, off, W, y=y)
+    torch.cuda.synchronize()
+    wq, dwq = oracle.q4_0_decode(blocks.reshape(E * n, k // 32, 18), k)
+    wq = wq.reshape(E, n, k)
+    dwq = dwq.reshape(E, n, k // 32)
+    rows = np.arange(total) if rows is None else rows
+    rr, cc = np.meshgrid(rows, np.arange(n), indexing="ij")
+    ref = oracle.grouped_points(q, d, offsets, wq, dwq, rr.ravel(), cc.ravel()).reshape(
+        len(rows), n)
+    yg = y.cpu().numpy()[rows]
+    err = row_rel_err(yg, ref)
+    assert err <= TOL and err <= TIGHT, err
+    return y, codes, scales, q, W, wq
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_grouped_moe512(torch, bits):
+    t = synth.make("moe512")
+    off = t["offsets"]
+    # rows across many experts, including the first and last rows of several
+    rows = np.unique(np.concatenate([sample_rows(4096, 40, seed=bits), off[1:-1:9],
+                                     off[1:-1:9] - 1]))
+    check_grouped(t["x_gu"], t["w_gu"], off, 1536, 2048, 128, bits, rows=rows, label="gate/up")
+    check_grouped(t["x_dn"], t["w_dn"], off, 2048, 768, 128, bits, rows=rows, label="down")
+
+
+def test_grouped_ragged_experts(torch):
+    rng = np.random.default_rng(41)
+    E, n, k = 6, 64, 128
+    counts = np.array([0, 1, 70, 0, 33, 129])            # empty, single, > 64, multi-slot
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    x, _ = synth.draw_activations(rng, int(off[-1]), k, "normal", 0.02, 20.0)
+    blocks = synth.draw_q4_0(rng, (E, n), k, 0.005, 0.05)
+    y, codes, scales, q, W, wq = check_grouped(x, blocks, off, n, k, E, 4, label="ragged")
+    # block sums through an expert's weights match too
+    check_blocksums(codes, scales, 4, W, q, wq[4], [(off[4], off[5], 0, 64)], expert=4)
+
+
+def test_grouped_leaves_rows_outside_experts(torch):
+    rng = np.random.default_rng(42)
+    E, n, k, rows = 2, 32, 64, 10
+    off = np.array([0, 3, 7], dtype=np.int32)           # rows 7..9 belong to no expert
+    x, _ = synth.draw_activations(rng, rows, k, "normal")
+    blocks = synth.draw_q4_0(rng, (E, n), k, 0.005, 0.05)
+    y, *_ = check_grouped(x, blocks, off, n, k, E, 4, rows=np.arange(7), label="partial")
+    assert np.all(np.isnan(y.cpu().numpy()[7:]))
+
+
+# ------------------------------------------------------------------ determinism
+
+def test_repeat_runs_are_bit_identical(torch):
+    t = synth.make("attn512")
+    xd = act_to_device(t["x"])
+    W = weights_to_device(t["w"], 5120, 5120)
+    outs = []
+    for _ in range(2):
+        codes, scales = bb.quantize_act_h32(xd, 4)
+        outs.append(bb.w4a4_gemm(codes, scales, 4, W).cpu().numpy().view(np.uint32))
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        codes, scales = bb.quantize_act_h32(xd, 4, stream=s)
+        y = bb.w4a4_gemm(codes, scales, 4, W, stream=s)
+    s.synchronize()
+    outs.append(y.cpu().numpy().view(np.uint32))
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])

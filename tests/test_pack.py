@@ -1,0 +1,61 @@
+"""rotate_pack_weights (host code of the library) against the documented image
+layout and, for float sources, bit-exact against the oracle's offline path."""
+import numpy as np
+import pytest
+
+import oracle
+from bit_prefill_gemm_amd import binding as bb
+from bit_prefill_gemm_amd import synth
+
+
+def unpack_image(img: np.ndarray, n: int, k: int, e: int) -> np.ndarray:
+    """Read the image back per its documented layout into canonical blocks [e, n, k/32, 18]."""
+    B = k // 32
+    codes = img[: e * n * B * 16].reshape(e, n // 32, B, 32, 16)
+    scales = img[e * n * B * 16:].view("<u2").reshape(e, n // 32, B, 32)
+    out = np.empty((e, n, B, 18), dtype=np.uint8)
+    for t in range(n // 32):
+        for j in range(32):
+            out[:, t * 32 + j, :, 2:] = codes[:, t, :, j, :]
+            out[:, t * 32 + j, :, 0:2] = scales[:, t, :, j].astype("<u2").view(np.uint8).reshape(
+                e, B, 2)
+    return out
+
+
+@pytest.mark.parametrize("n,k,e", [(32, 32, 1), (96, 160, 1), (64, 256, 3)])
+def test_q4_0_source_is_relaid_out_verbatim(n, k, e):
+    blocks = synth.draw_q4_0(np.random.default_rng(n + k + e), (e, n), k, 0.002, 0.02)
+    W = bb.rotate_pack_weights(blocks, bb.SRC_Q4_0_ROTATED, n, k, e)
+    assert W.desc.rotation == 32 and W.desc.num_experts == e
+    assert np.array_equal(unpack_image(W.image, n, k, e), blocks)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_float_source_matches_oracle_bit_exact(dtype):
+    rng = np.random.default_rng(21)
+    n, k, e = 64, 320, 2
+    w = rng.standard_normal((e * n, k)).astype(np.float32) * 0.03
+    w[:, rng.choice(k, 6, replace=False)] *= 12.0          # outlier input channels
+    w[3, 32:64] = 0.0                                       # an all-zero block
+    w[5, 64:96] = 1e-6                                      # a tiny constant block
+    src = w if dtype == "f32" else synth.bf16_bits(w)
+    kind = bb.SRC_F32 if dtype == "f32" else bb.SRC_BF16
+    W = bb.rotate_pack_weights(src, kind, n, k, e)
+    got = unpack_image(W.image, n, k, e).reshape(e * n, k // 32, 18)
+    ref = oracle.quantize_weights_q4_0(src, rotate=True)
+    assert np.array_equal(got, ref)
+
+
+def test_float_source_reproduces_unrotated_product():
+    """Packed float weights stand for H w / sqrt(32): the route's product is x . w."""
+    rng = np.random.default_rng(22)
+    n, k = 32, 128
+    w = rng.standard_normal((n, k)).astype(np.float32) * 0.05
+    W = bb.rotate_pack_weights(w, bb.SRC_F32, n, k, 1)
+    blocks = unpack_image(W.image, n, k, 1)[0]
+    wq, dw = oracle.q4_0_decode(blocks, k)
+    x = rng.standard_normal((4, k)).astype(np.float32)
+    rows, cols = np.meshgrid(np.arange(4), np.arange(n), indexing="ij")
+    y = oracle.ref_points(x, wq, dw, rows.ravel(), cols.ravel()).reshape(4, n)
+    exact = x.astype(np.float64) @ w.astype(np.float64).T
+    assert np.linalg.norm(y - exact) / np.linalg.norm(exact) < 0.1
