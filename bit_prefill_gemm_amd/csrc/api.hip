@@ -87,7 +87,8 @@ bpg_status check_act(const void *codes, const float *scales, int act_bits, int64
         return BPG_ERR_DTYPE;
     if (rows < 0 || rows > ((int64_t)1 << 31) - 1)
         return BPG_ERR_SHAPE;
-    if (!codes || !scales)
+    // with no rows nothing is read, and empty tensors may carry NULL pointers
+    if (rows > 0 && (!codes || !scales))
         return BPG_ERR_NULL;
     if (!aligned16(codes) || !aligned16(scales))
         return BPG_ERR_ALIGN;
@@ -257,7 +258,7 @@ bpg_status quantize_act_h32(const void *x, bpg_x_dtype dt, int64_t m, int64_t k,
     if (m < 0 || k <= 0 || k % 32 != 0 || ldx < k || m > ((int64_t)1 << 31) - 1 ||
         k > ((int64_t)1 << 30) || ldx > ((int64_t)1 << 40))
         return BPG_ERR_SHAPE;
-    if (!x || !codes || !scales)
+    if (m > 0 && (!x || !codes || !scales))
         return BPG_ERR_NULL;
     if (!aligned16(x) || !aligned16(codes) || !aligned16(scales) || ldx % 4 != 0)
         return BPG_ERR_ALIGN;
@@ -284,7 +285,7 @@ bpg_status w4a4_gemm(const void *codes, const float *scales, int act_bits, int64
         return s;
     if (ldy < w->n)
         return BPG_ERR_SHAPE;
-    if (!w_dev || !y)
+    if (!w_dev || (m > 0 && !y))
         return BPG_ERR_NULL;
     if (!aligned16(w_dev) || !aligned16(y) || ldy % 4 != 0)
         return BPG_ERR_ALIGN;
@@ -321,7 +322,7 @@ bpg_status w4a4_grouped_gemm(const void *codes, const float *scales, int act_bit
         return s;
     if (ldy < w->n)
         return BPG_ERR_SHAPE;
-    if (!w_dev || !y || !expert_offsets_dev)
+    if (!w_dev || !expert_offsets_dev || (total_rows > 0 && !y))
         return BPG_ERR_NULL;
     if (!aligned16(w_dev) || !aligned16(y) || ldy % 4 != 0 ||
         (reinterpret_cast<uintptr_t>(expert_offsets_dev) & 3u) != 0)

@@ -4,28 +4,32 @@
 // prompts are a matrix-unit problem": prompts are a matrix-unit workload; a
 // Q4_0 code u means u-8, which is the code with its top bit flipped read as a
 // 4-bit two's-complement number, so the kernel reads Q4_0 nibbles bit for bit.
-// gfx950 has no int4 matrix instruction, so both operands are widened to int8
-// in registers and each 32-value block is one v_mfma_i32_32x32x32_i8 per
-// 32x32 output tile.
+// gfx950 has no int4 matrix instruction: both operands are widened to int8 in
+// registers and every 32-value block is one v_mfma_i32_16x16x32_i8 per 16x16
+// output tile (K = 32 is exactly one block, so each result is one block sum).
 //
 // Per K-block b the kernel needs y[m][n] += da[m][b] * dw[n][b] * S[m][n][b]
 // with S the exact int32 block dot product:
-//   - operands are widened as 16*value (a nibble in the top half of a byte),
+//   - operands are widened as 16*value (the nibble in the top half of a byte),
 //     so the instruction returns 256*S (8-bit activations: 16*S); the power
-//     of two is folded into the weight scale;
+//     of two is removed once, when the output is stored;
 //   - the accumulator input is 0x4B400000 (1.5*2^23 as fp32), so the int32
-//     result, read as fp32, is exactly 12582912 + 256*S (|256*S| < 2^22);
-//   - t = fma(F, dws, -12582912*dws) = 256*S*dws (the constant product is exact
-//     because dws carries at most 11 significant bits), then
-//     acc = fma(t, da, acc).
-// That is two fp32 VALU operations per (m, n, b) and no integer conversion.
-// The block sums themselves are exposed through the same main loop
-// (MODE kSums) for bit-exact parity checks.
+//     result read as fp32 is exactly 12582912 + 256*S (|256*S| < 2^22);
+//   - t = fma(F, dw, -12582912*dw) = 256*S*dw (the constant product is exact:
+//     dw is an fp16 value, 11 significant bits), then acc = fma(t, da, acc).
+// Two fp32 VALU operations per (m, n, b) and no integer conversion.  Packed
+// fp32 is not used, so that epilogue, not the matrix core, bounds the kernel:
+// one 16x16x32 instruction yields 256 sums = 8 VALU instructions per wave.
 //
-// Data flow: activation codes [rows][k/2] (or [rows][k]) and the weight image
-// ([N/32][B][32][16 B] nibbles + fp16 scales) are staged through LDS, KC
-// blocks per stage, double buffered, laid out so that every wave reads its
-// MFMA operands as one contiguous 512-byte run per instruction.
+// Work split: a workgroup owns a BM x BN output tile; its 4 waves each take
+// every 4th K-block of a stage and keep partial sums of the whole tile, which
+// are added in a fixed order (wave 0, 1, 2, 3) through LDS at the end, so the
+// result is bit-identical from run to run.  Operands are staged through LDS,
+// KC blocks per stage, double buffered, with the next stage's global loads in
+// flight during the current stage's arithmetic.  Two workgroups fit on a CU.
+//
+// The same main loop also runs in block-sum mode (exact int32 S for parity
+// checks) and in grouped mode (rows sorted by expert, ragged row ranges).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -36,57 +40,55 @@ namespace bpg {
 namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
-typedef int v16i __attribute__((ext_vector_type(16)));
 
 constexpr int kMagicBits = 0x4B400000;
 constexpr float kMagic = 12582912.0f;
 
 enum Mode { kGemm = 0, kGrouped = 1, kSums = 2 };
 
-template <int BITS_, int BM_, int BN_, int KC_, int WM_, int WN_, int WK_>
+template <int BITS_, int BM_, int BN_, int KC_>
 struct Cfg {
     static constexpr int BITS = BITS_, BM = BM_, BN = BN_, KC = KC_;
-    static constexpr int WM = WM_, WN = WN_, WK = WK_;
-    static constexpr int kWaves = WM * WN * WK;
+    static constexpr int kWaves = 4;
     static constexpr int kThreads = 64 * kWaves;
-    static constexpr int TM = BM / (32 * WM);
-    static constexpr int TN = BN / (32 * WN);
-    static constexpr int kAB = BITS == 4 ? 16 : 32;  // activation code bytes per (row, block)
-    static constexpr int kShift = BITS == 4 ? 8 : 4; // log2 of the operand widening factor
+    static constexpr int TM = BM / 16, TN = BN / 16;
+    static constexpr int kAB = BITS == 4 ? 16 : 32;   // code bytes per (row, block)
+    static constexpr int kShift = BITS == 4 ? 8 : 4;  // log2 of the operand widening
+    // one stage in LDS: A codes [KC][BM][kAB], W codes [KC][BN][16],
+    // row scales [KC][BM] fp32, column scales [KC][BN] (dw, -12582912*dw)
     static constexpr int kLdsA = KC * BM * kAB;
     static constexpr int kLdsW = KC * BN * 16;
-    static constexpr int kLdsAs = KC * BM * 4;
-    static constexpr int kLdsWs = KC * BN * 8;
-    static constexpr int kLdsBuf = kLdsA + kLdsW + kLdsAs + kLdsWs;
-    static constexpr int kLdsRed = WM * WN * (WK - 1) * 1024 * 4;
-    static constexpr int kLds = (2 * kLdsBuf > kLdsRed ? 2 * kLdsBuf : kLdsRed);
-    static constexpr int kChunksA = BM * KC * (kAB / 16); // 16-byte chunks per stage
-    static constexpr int kChunksW = BN * KC;
-    static constexpr int kPerThreadA = (kChunksA + kThreads - 1) / kThreads;
-    static constexpr int kPerThreadW = (kChunksW + kThreads - 1) / kThreads;
-    static_assert(BM % (32 * WM) == 0 && BN % (32 * WN) == 0, "wave tiling");
-    static_assert(KC % WK == 0, "K split");
-    static_assert(kLds <= 65536, "LDS budget");
+    static constexpr int kLdsDa = KC * BM * 4;
+    static constexpr int kLdsDw = KC * BN * 8;
+    static constexpr int kStage = kLdsA + kLdsW + kLdsDa + kLdsDw;
+    static constexpr int kTiles = TM * TN;
+    // final reduction: every wave parks the partial sums of up to kRedTiles
+    // tiles at a time ([wave][tile][4 regs][64 lanes] fp32)
+    static constexpr int kRedTiles = kTiles < 16 ? kTiles : 16;
+    static constexpr int kLdsRed = kWaves * kRedTiles * 4 * 64 * 4;
+    static constexpr int kLds = 2 * kStage > kLdsRed ? 2 * kStage : kLdsRed;
+    // 16-byte global chunks per stage and per thread
+    static constexpr int kChA = BM * KC * (kAB / 16);
+    static constexpr int kChW = BN * KC;
+    static constexpr int kPtA = (kChA + kThreads - 1) / kThreads;
+    static constexpr int kPtW = (kChW + kThreads - 1) / kThreads;
+    static constexpr int kPtDa = (BM * KC + kThreads - 1) / kThreads;
+    static constexpr int kPtDw = (BN * KC + kThreads - 1) / kThreads;
+    static_assert(BM % 16 == 0 && BN % 16 == 0 && KC % kWaves == 0, "tiling");
+    static_assert(kLds <= 160 * 1024, "LDS budget");
 };
 
-// Activation nibbles (already two's complement) -> 16*value in each byte.
-__device__ __forceinline__ v4i widen_act4(uint2 r)
+// Activation nibbles (two's complement) of one dword -> 8 int8 = 16 * value:
+// low nibbles (elements 4g..4g+3) then high nibbles (elements 16+4g..16+4g+3).
+__device__ __forceinline__ long widen_act4(uint32_t d)
 {
-    v4i o;
-    o[0] = (int)((r.x << 4) & 0xF0F0F0F0u);
-    o[1] = (int)((r.y << 4) & 0xF0F0F0F0u);
-    o[2] = (int)(r.x & 0xF0F0F0F0u);
-    o[3] = (int)(r.y & 0xF0F0F0F0u);
-    return o;
+    const uint32_t lo = (d << 4) & 0xF0F0F0F0u;
+    const uint32_t hi = d & 0xF0F0F0F0u;
+    return (long)(((uint64_t)hi << 32) | lo);
 }
 
-// Q4_0 nibbles u -> top bit flipped (u XOR 8 = u-8 in two's complement) -> 16*(u-8).
-__device__ __forceinline__ v4i widen_q4_0(uint2 r)
-{
-    r.x ^= 0x88888888u;
-    r.y ^= 0x88888888u;
-    return widen_act4(r);
-}
+// Q4_0 nibbles u -> top bit flipped (u XOR 8 is u-8 in two's complement) -> 16*(u-8).
+__device__ __forceinline__ long widen_q4_0(uint32_t d) { return widen_act4(d ^ 0x88888888u); }
 
 __device__ __forceinline__ float half_bits_to_float(uint16_t h)
 {
@@ -94,8 +96,8 @@ __device__ __forceinline__ float half_bits_to_float(uint16_t h)
 }
 
 // Workgroups are dispatched round-robin over the 8 XCDs (w % 8 selects the
-// XCD).  Hand each XCD a contiguous range of logical tiles so that the tiles
-// sharing weight columns share that XCD's L2.
+// XCD).  Hand each XCD a contiguous range of logical tiles, so tiles that
+// share weight columns share that XCD's L2.
 __device__ __forceinline__ int xcd_remap(int w, int total)
 {
     if (total % 8 != 0)
@@ -157,26 +159,23 @@ __device__ bool grouped_slot(const int32_t *__restrict__ off, int64_t experts, i
 }
 
 template <class C, int MODE>
-__global__ __launch_bounds__(C::kThreads) void w4a4_kernel(GemmProblem p, int tiles_m,
-                                                           int tiles_n, int tm0, int tn0)
+__global__ __launch_bounds__(C::kThreads, 2) void w4a4_kernel(GemmProblem p, int tiles_m,
+                                                              int tiles_n, int tm0, int tn0)
 {
     constexpr int BM = C::BM, BN = C::BN, KC = C::KC, TM = C::TM, TN = C::TN;
-    constexpr int WN = C::WN, WK = C::WK, NT = C::kThreads, kAB = C::kAB;
+    constexpr int NT = C::kThreads, kAB = C::kAB, WAVES = C::kWaves;
     __shared__ __attribute__((aligned(16))) uint8_t lds[C::kLds];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int rr = lane & 31;
-    const int g = lane >> 5;
+    const int j16 = lane & 15; // row (A operand) / column (B operand, output) in a 16-tile
+    const int g = lane >> 4;   // K group of the operands; output rows 4g..4g+3
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wk = wave % WK;
-    const int wn = (wave / WK) % WN;
-    const int wm = wave / (WK * WN);
 
     const int64_t B = p.k / 32;
     const int64_t ntiles32 = p.n / 32;
 
-    // ---- which tile this workgroup computes
+    // ---- the tile of this workgroup
     const int L = xcd_remap(blockIdx.x, gridDim.x);
     int64_t row0, row_end, col0, expert;
     if (MODE == kGrouped) {
@@ -185,157 +184,150 @@ __global__ __launch_bounds__(C::kThreads) void w4a4_kernel(GemmProblem p, int ti
         if (!grouped_slot<NT>(p.offsets, p.experts, p.rows, BM, slot,
                               reinterpret_cast<int *>(lds), row0, row_end, expert))
             return; // uniform across the workgroup
-        __syncthreads(); // the scan area is reused by the stage buffers below
     } else {
         row0 = (int64_t)(tm0 + L % tiles_m) * BM;
         col0 = (int64_t)(tn0 + L / tiles_m) * BN;
         row_end = p.rows;
         expert = MODE == kSums ? p.expert : 0;
     }
-
-    const uint8_t *__restrict__ wc = p.wcodes + expert * ntiles32 * B * 512;
-    const uint16_t *__restrict__ ws = p.wscales + expert * ntiles32 * B * 32;
-    const int64_t ct0 = col0 / 32;
     const int64_t arow_bytes = p.k * kAB / 32;
+    const int64_t ct0 = col0 >> 5; // first 32-column image tile touched by this tile
 
-    // ---- staging registers
-    uint4 ra[C::kPerThreadA];
-    uint4 rw[C::kPerThreadW];
-    constexpr int kPerThreadAs = (BM * KC + NT - 1) / NT;
-    constexpr int kPerThreadWs = (BN * KC + NT - 1) / NT;
-    float ras[kPerThreadAs];
-    uint16_t rws[kPerThreadWs];
+    // ---- staging addresses, computed once.  Global reads are coalesced
+    //      (consecutive threads read consecutive blocks of a row, or
+    //      consecutive columns); LDS slots are XOR-swizzled so that both these
+    //      writes and the MFMA operand reads spread over all banks.  Rows past
+    //      row_end are clamped to the last valid row: their values only reach
+    //      output rows that are never stored.
+    const uint8_t *__restrict__ a_base0 = p.codes + row0 * arow_bytes;
+    const uint8_t *__restrict__ w_base0 = p.wcodes + (expert * ntiles32 + ct0) * B * 512;
+    const float *__restrict__ da_base0 = p.scales + row0 * B;
+    const uint16_t *__restrict__ dw_base0 = p.wscales + (expert * ntiles32 + ct0) * B * 32;
+    const int last_row = (int)(row_end - 1 - row0); // >= 0
 
+    uint32_t oa[C::kPtA], la[C::kPtA], ow[C::kPtW], lw[C::kPtW];
+    uint32_t oda[C::kPtDa], lda_[C::kPtDa], odw[C::kPtDw], ldw_[C::kPtDw];
+    int8_t kca[C::kPtA], kcw[C::kPtW], kcda[C::kPtDa], kcdw[C::kPtDw]; // block of each chunk
+#pragma unroll
+    for (int i = 0; i < C::kPtA; i++) {
+        const int c = tid + i * NT;
+        const int cc = c < C::kChA ? c : 0;
+        const int row = cc / (KC * (kAB / 16));
+        const int rem = cc % (KC * (kAB / 16));
+        const int kc = rem / (kAB / 16), part = rem % (kAB / 16);
+        const int rrow = row < last_row ? row : last_row;
+        oa[i] = (uint32_t)(rrow * arow_bytes + kc * kAB + part * 16);
+        const int srow = kAB == 16 ? (row ^ kc ^ ((row & 1) << 3)) : (row ^ kc);
+        const int slot = kAB == 32 ? (part ^ ((srow >> 3) & 1)) : 0;
+        la[i] = (uint32_t)((kc * BM + srow) * kAB + slot * 16);
+        kca[i] = (int8_t)(c < C::kChA ? kc : 127);
+    }
+#pragma unroll
+    for (int i = 0; i < C::kPtW; i++) {
+        const int c = tid + i * NT;
+        const int cc = c < C::kChW ? c : 0;
+        const int col = cc / KC, kc = cc % KC;
+        const int64_t gcol = col0 + col;
+        ow[i] = (uint32_t)((((gcol >> 5) - ct0) * B + kc) * 512 + (gcol & 31) * 16);
+        lw[i] = (uint32_t)((kc * BN + (col ^ kc ^ ((col & 1) << 3))) * 16);
+        kcw[i] = (int8_t)(c < C::kChW ? kc : 127);
+    }
+#pragma unroll
+    for (int i = 0; i < C::kPtDa; i++) {
+        const int c = tid + i * NT;
+        const int cc = c < BM * KC ? c : 0;
+        const int kc = cc / BM, row = cc % BM;
+        const int rrow = row < last_row ? row : last_row;
+        oda[i] = (uint32_t)(rrow * B + kc);
+        lda_[i] = (uint32_t)(kc * BM + row);
+        kcda[i] = (int8_t)(c < BM * KC ? kc : 127);
+    }
+#pragma unroll
+    for (int i = 0; i < C::kPtDw; i++) {
+        const int c = tid + i * NT;
+        const int cc = c < BN * KC ? c : 0;
+        const int kc = cc / BN, col = cc % BN;
+        const int64_t gcol = col0 + col;
+        odw[i] = (uint32_t)((((gcol >> 5) - ct0) * B + kc) * 32 + (gcol & 31));
+        ldw_[i] = (uint32_t)(kc * BN + col);
+        kcdw[i] = (int8_t)(c < BN * KC ? kc : 127);
+    }
+
+    // ---- global -> registers -> LDS staging of one stage (KC blocks)
+    uint4 ra[C::kPtA], rw[C::kPtW];
+    float rda[C::kPtDa];
+    uint16_t rdw[C::kPtDw];
+
+    // Loads of blocks past K (only in a last, partial stage) are skipped.
     auto load_stage = [&](int64_t kb0) {
+        const int kv = (int)(B - kb0 < KC ? B - kb0 : KC);
+        const uint8_t *ab = a_base0 + kb0 * kAB;
+        const uint8_t *wb = w_base0 + kb0 * 512;
+        const float *dab = da_base0 + kb0;
+        const uint16_t *dwb = dw_base0 + kb0 * 32;
 #pragma unroll
-        for (int i = 0; i < C::kPerThreadA; i++) {
-            const int c = tid + i * NT;
-            uint4 v = make_uint4(0, 0, 0, 0);
-            if (c < C::kChunksA) {
-                const int row = c / (KC * (kAB / 16));
-                const int rem = c % (KC * (kAB / 16));
-                const int kc = rem / (kAB / 16), part = rem % (kAB / 16);
-                const int64_t grow = row0 + row;
-                if (grow < row_end && kb0 + kc < B)
-                    v = *reinterpret_cast<const uint4 *>(p.codes + grow * arow_bytes +
-                                                         (kb0 + kc) * kAB + part * 16);
-            }
-            ra[i] = v;
-        }
+        for (int i = 0; i < C::kPtA; i++)
+            ra[i] = kca[i] < kv ? *reinterpret_cast<const uint4 *>(ab + oa[i]) : make_uint4(0, 0, 0, 0);
 #pragma unroll
-        for (int i = 0; i < C::kPerThreadW; i++) {
-            const int c = tid + i * NT;
-            uint4 v = make_uint4(0, 0, 0, 0);
-            if (c < C::kChunksW) {
-                const int ct = c / (KC * 32);
-                const int rem = c % (KC * 32);
-                const int kc = rem / 32, j = rem % 32;
-                if (kb0 + kc < B)
-                    v = *reinterpret_cast<const uint4 *>(
-                        wc + (((ct0 + ct) * B + kb0 + kc) * 32 + j) * 16);
-            }
-            rw[i] = v;
-        }
+        for (int i = 0; i < C::kPtW; i++)
+            rw[i] = kcw[i] < kv ? *reinterpret_cast<const uint4 *>(wb + ow[i]) : make_uint4(0, 0, 0, 0);
+        if (MODE != kSums) { // block sums never read scales
 #pragma unroll
-        for (int i = 0; i < kPerThreadAs; i++) {
-            const int c = tid + i * NT;
-            float v = 0.0f;
-            if (c < BM * KC) {
-                const int row = c / KC, kc = c % KC;
-                const int64_t grow = row0 + row;
-                if (MODE != kSums && grow < row_end && kb0 + kc < B)
-                    v = p.scales[grow * B + kb0 + kc]; // block sums never read scales
-            }
-            ras[i] = v;
-        }
+            for (int i = 0; i < C::kPtDa; i++)
+                rda[i] = kcda[i] < kv ? dab[oda[i]] : 0.0f;
 #pragma unroll
-        for (int i = 0; i < kPerThreadWs; i++) {
-            const int c = tid + i * NT;
-            uint16_t v = 0;
-            if (c < BN * KC) {
-                const int ct = c / (KC * 32);
-                const int rem = c % (KC * 32);
-                const int kc = rem / 32, j = rem % 32;
-                if (kb0 + kc < B)
-                    v = ws[((ct0 + ct) * B + kb0 + kc) * 32 + j];
-            }
-            rws[i] = v;
+            for (int i = 0; i < C::kPtDw; i++)
+                rdw[i] = kcdw[i] < kv ? dwb[odw[i]] : (uint16_t)0;
         }
     };
 
     auto store_stage = [&](int buf) {
-        uint8_t *A = lds + buf * C::kLdsBuf;
+        uint8_t *A = lds + buf * C::kStage;
         uint8_t *W = A + C::kLdsA;
-        float *As = reinterpret_cast<float *>(W + C::kLdsW);
-        float2 *Ws = reinterpret_cast<float2 *>(W + C::kLdsW + C::kLdsAs);
+        float *Da = reinterpret_cast<float *>(W + C::kLdsW);
+        float2 *Dw = reinterpret_cast<float2 *>(W + C::kLdsW + C::kLdsDa);
 #pragma unroll
-        for (int i = 0; i < C::kPerThreadA; i++) {
-            const int c = tid + i * NT;
-            if (c < C::kChunksA) {
-                const int row = c / (KC * (kAB / 16));
-                const int rem = c % (KC * (kAB / 16));
-                const int kc = rem / (kAB / 16), part = rem % (kAB / 16);
-                const int rt = row / 32, r = row % 32;
-                const int base = (kc * (BM / 32) + rt) * (kAB / 8) + part * 2;
-                *reinterpret_cast<uint2 *>(A + base * 256 + r * 8) = make_uint2(ra[i].x, ra[i].y);
-                *reinterpret_cast<uint2 *>(A + (base + 1) * 256 + r * 8) =
-                    make_uint2(ra[i].z, ra[i].w);
-            }
-        }
+        for (int i = 0; i < C::kPtA; i++)
+            if (kca[i] < KC)
+                *reinterpret_cast<uint4 *>(A + la[i]) = ra[i];
 #pragma unroll
-        for (int i = 0; i < C::kPerThreadW; i++) {
-            const int c = tid + i * NT;
-            if (c < C::kChunksW) {
-                const int ct = c / (KC * 32);
-                const int rem = c % (KC * 32);
-                const int kc = rem / 32, j = rem % 32;
-                const int base = (kc * (BN / 32) + ct) * 2;
-                *reinterpret_cast<uint2 *>(W + base * 256 + j * 8) = make_uint2(rw[i].x, rw[i].y);
-                *reinterpret_cast<uint2 *>(W + (base + 1) * 256 + j * 8) =
-                    make_uint2(rw[i].z, rw[i].w);
-            }
-        }
+        for (int i = 0; i < C::kPtW; i++)
+            if (kcw[i] < KC)
+                *reinterpret_cast<uint4 *>(W + lw[i]) = rw[i];
+        if (MODE != kSums) {
 #pragma unroll
-        for (int i = 0; i < kPerThreadAs; i++) {
-            const int c = tid + i * NT;
-            if (c < BM * KC) {
-                const int row = c / KC, kc = c % KC;
-                As[kc * BM + row] = ras[i];
-            }
-        }
+            for (int i = 0; i < C::kPtDa; i++)
+                if (kcda[i] < KC)
+                    Da[lda_[i]] = rda[i];
 #pragma unroll
-        for (int i = 0; i < kPerThreadWs; i++) {
-            const int c = tid + i * NT;
-            if (c < BN * KC) {
-                const int ct = c / (KC * 32);
-                const int rem = c % (KC * 32);
-                const int kc = rem / 32, j = rem % 32;
-                const float dws = half_bits_to_float(rws[i]) * (1.0f / (1 << C::kShift));
-                Ws[kc * BN + ct * 32 + j] = make_float2(dws, -kMagic * dws);
-            }
+            for (int i = 0; i < C::kPtDw; i++)
+                if (kcdw[i] < KC) {
+                    const float dw = half_bits_to_float(rdw[i]);
+                    Dw[ldw_[i]] = make_float2(dw, -kMagic * dw);
+                }
         }
     };
 
-    // rows of each of this wave's 32-row tiles that hold data (wave-uniform)
+    // 16-row tiles of the workgroup tile that hold data (uniform per workgroup)
     int vrows[TM];
 #pragma unroll
     for (int i = 0; i < TM; i++) {
-        int64_t v = row_end - (row0 + (int64_t)(wm * TM + i) * 32);
-        vrows[i] = v < 0 ? 0 : (v > 32 ? 32 : (int)v);
+        const int64_t v = row_end - (row0 + (int64_t)i * 16);
+        vrows[i] = v < 0 ? 0 : (v > 16 ? 16 : (int)v);
     }
 
-    float acc[TM][TN][16];
+    float acc[TM][TN][4];
 #pragma unroll
     for (int i = 0; i < TM; i++)
 #pragma unroll
         for (int j = 0; j < TN; j++)
 #pragma unroll
-            for (int r = 0; r < 16; r++)
+            for (int r = 0; r < 4; r++)
                 acc[i][j][r] = 0.0f;
 
-    v16i magic;
+    v4i magic;
 #pragma unroll
-    for (int r = 0; r < 16; r++)
+    for (int r = 0; r < 4; r++)
         magic[r] = kMagicBits;
 
     const int64_t nstages = (B + KC - 1) / KC;
@@ -349,89 +341,90 @@ __global__ __launch_bounds__(C::kThreads) void w4a4_kernel(GemmProblem p, int ti
         if (s + 1 < nstages)
             load_stage(kb0 + KC);
 
-        const uint8_t *A = lds + buf * C::kLdsBuf;
+        const uint8_t *A = lds + buf * C::kStage;
         const uint8_t *W = A + C::kLdsA;
-        const float *As = reinterpret_cast<const float *>(W + C::kLdsW);
-        const float2 *Ws = reinterpret_cast<const float2 *>(W + C::kLdsW + C::kLdsAs);
-        const int64_t kvalid = B - kb0; // blocks of this stage inside K (>= 1)
+        const float *Da = reinterpret_cast<const float *>(W + C::kLdsW);
+        const float2 *Dw = reinterpret_cast<const float2 *>(W + C::kLdsW + C::kLdsDa);
+        const int64_t kvalid = B - kb0; // >= 1
 
 #pragma unroll
-        for (int kk = 0; kk < KC / WK; kk++) {
-            const int kc = kk * WK + wk;
+        for (int kk = 0; kk < KC / WAVES; kk++) {
+            const int kc = kk * WAVES + wave;
             if (kc >= kvalid)
                 break;
-            v4i a[TM], b[TN];
+            // A operands: row j16 of each 16-row tile, K group g
+            // swizzled slot of row/column j16 of every 16-tile for this block
+            const int sw16 = kAB == 16 ? (j16 ^ kc ^ ((j16 & 1) << 3)) : (j16 ^ kc);
+            const int swc = j16 ^ kc ^ ((j16 & 1) << 3);
+            long a[TM];
 #pragma unroll
             for (int i = 0; i < TM; i++) {
-                const int base = (kc * (BM / 32) + wm * TM + i) * (kAB / 8);
-                if (C::BITS == 4) {
-                    a[i] = widen_act4(*reinterpret_cast<const uint2 *>(A + (base + g) * 256 + rr * 8));
+                if (kAB == 16) {
+                    a[i] = widen_act4(*reinterpret_cast<const uint32_t *>(A + (kc * BM + i * 16 + sw16) * 16 + 4 * g));
                 } else {
-                    uint2 lo = *reinterpret_cast<const uint2 *>(A + (base + g) * 256 + rr * 8);
-                    uint2 hi = *reinterpret_cast<const uint2 *>(A + (base + 2 + g) * 256 + rr * 8);
-                    a[i][0] = (int)lo.x; a[i][1] = (int)lo.y;
-                    a[i][2] = (int)hi.x; a[i][3] = (int)hi.y;
+                    const int srow = i * 16 + sw16;
+                    const int sw = (srow >> 3) & 1;
+                    const uint32_t lo = *reinterpret_cast<const uint32_t *>(A + (kc * BM + srow) * 32 + (sw * 16) + 4 * g);
+                    const uint32_t hi = *reinterpret_cast<const uint32_t *>(A + (kc * BM + srow) * 32 + ((sw ^ 1) * 16) + 4 * g);
+                    a[i] = (long)(((uint64_t)hi << 32) | lo);
                 }
             }
-#pragma unroll
-            for (int j = 0; j < TN; j++) {
-                const int base = (kc * (BN / 32) + wn * TN + j) * 2;
-                b[j] = widen_q4_0(*reinterpret_cast<const uint2 *>(W + (base + g) * 256 + rr * 8));
-            }
-
-            v16i D[TM][TN];
-#pragma unroll
-            for (int i = 0; i < TM; i++)
-#pragma unroll
-                for (int j = 0; j < TN; j++)
-                    if (vrows[i] > 0)
-                        D[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[i], b[j], magic, 0, 0, 0);
 
             if (MODE == kSums) {
 #pragma unroll
+                for (int j = 0; j < TN; j++) {
+                    const long b = widen_q4_0(*reinterpret_cast<const uint32_t *>(W + (kc * BN + j * 16 + swc) * 16 + 4 * g));
+                    const int64_t col = col0 + j * 16 + j16;
+#pragma unroll
+                    for (int i = 0; i < TM; i++) {
+                        const v4i D = __builtin_amdgcn_mfma_i32_16x16x32_i8(a[i], b, magic, 0, 0, 0);
+#pragma unroll
+                        for (int r = 0; r < 4; r++) {
+                            const int64_t row = row0 + i * 16 + 4 * g + r;
+                            if (row >= p.m0 && row < p.m1 && col >= p.n0 && col < p.n1)
+                                p.sums[((row - p.m0) * (p.n1 - p.n0) + (col - p.n0)) * B + kb0 + kc] =
+                                    (D[r] - kMagicBits) >> C::kShift;
+                        }
+                    }
+                }
+            } else {
+                float4 da[TM];
+#pragma unroll
                 for (int i = 0; i < TM; i++)
+                    da[i] = *reinterpret_cast<const float4 *>(Da + kc * BM + i * 16 + 4 * g);
+                // Software pipeline over the column tiles: the matrix
+                // instructions of tile j are issued before the epilogue of
+                // tile j-1, so their latency hides behind VALU work.  Padded
+                // rows (past row_end) are computed too and never stored.
+                v4i Dp[TM];
+                float2 dwp = make_float2(0.0f, 0.0f);
 #pragma unroll
-                    for (int j = 0; j < TN; j++) {
-                        if (vrows[i] <= 0)
-                            continue;
-                        const int64_t col = col0 + (wn * TN + j) * 32 + rr;
+                for (int j = 0; j <= TN; j++) {
+                    v4i Dc[TM];
+                    float2 dwc = make_float2(0.0f, 0.0f);
+                    if (j < TN) {
+                        const long b = widen_q4_0(*reinterpret_cast<const uint32_t *>(W + (kc * BN + j * 16 + swc) * 16 + 4 * g));
+                        dwc = Dw[kc * BN + j * 16 + j16];
 #pragma unroll
-                        for (int r = 0; r < 16; r++) {
-                            const int64_t row = row0 + (wm * TM + i) * 32 + 8 * (r / 4) + 4 * g + (r % 4);
-                            if (row >= p.m0 && row < p.m1 && col >= p.n0 && col < p.n1) {
-                                const int32_t sv = (D[i][j][r] - kMagicBits) >> C::kShift;
-                                p.sums[((row - p.m0) * (p.n1 - p.n0) + (col - p.n0)) * B + kb0 + kc] = sv;
+                        for (int i = 0; i < TM; i++)
+                            Dc[i] = __builtin_amdgcn_mfma_i32_16x16x32_i8(a[i], b, magic, 0, 0, 0);
+                    }
+                    if (j > 0) {
+#pragma unroll
+                        for (int i = 0; i < TM; i++) {
+                            const float dq[4] = {da[i].x, da[i].y, da[i].z, da[i].w};
+#pragma unroll
+                            for (int r = 0; r < 4; r++) {
+                                const float t = __builtin_fmaf(__int_as_float(Dp[i][r]), dwp.x, dwp.y);
+                                acc[i][j - 1][r] = __builtin_fmaf(t, dq[r], acc[i][j - 1][r]);
                             }
                         }
                     }
-            } else {
-                float2 wsc[TN];
+                    if (j < TN) {
 #pragma unroll
-                for (int j = 0; j < TN; j++)
-                    wsc[j] = Ws[kc * BN + (wn * TN + j) * 32 + rr];
-#pragma unroll
-                for (int i = 0; i < TM; i++) {
-                    if (vrows[i] <= 0)
-                        continue;
-                    float4 da[4];
-#pragma unroll
-                    for (int q = 0; q < 4; q++)
-                        da[q] = *reinterpret_cast<const float4 *>(
-                            As + kc * BM + (wm * TM + i) * 32 + 8 * q + 4 * g);
-#pragma unroll
-                    for (int j = 0; j < TN; j++) {
-#pragma unroll
-                        for (int q = 0; q < 4; q++) {
-                            if (8 * q >= vrows[i])
-                                continue;
-                            const float dq[4] = {da[q].x, da[q].y, da[q].z, da[q].w};
-#pragma unroll
-                            for (int e = 0; e < 4; e++) {
-                                const int r = 4 * q + e;
-                                const float t = __builtin_fmaf(__int_as_float(D[i][j][r]), wsc[j].x, wsc[j].y);
-                                acc[i][j][r] = __builtin_fmaf(t, dq[e], acc[i][j][r]);
-                            }
-                        }
+                        for (int i = 0; i < TM; i++)
+                            Dp[i] = Dc[i];
+                        dwp = dwc;
                     }
                 }
             }
@@ -445,48 +438,37 @@ __global__ __launch_bounds__(C::kThreads) void w4a4_kernel(GemmProblem p, int ti
     if (MODE == kSums)
         return;
 
-    // ---- deterministic reduction of the K split: wave wk=0 adds wk=1,2,... in order
-    if (WK > 1) {
-        float *red = reinterpret_cast<float *>(lds);
-        const int grp = wm * WN + wn;
+    // ---- fixed-order sum of the four waves' partials; each wave stores a
+    //      quarter of the tiles.  The widening factor 2^kShift is removed here.
+    const float unscale = 1.0f / (float)(1 << C::kShift);
+    float *red = reinterpret_cast<float *>(lds);
+    for (int t0 = 0; t0 < C::kTiles; t0 += C::kRedTiles) {
 #pragma unroll
-        for (int i = 0; i < TM; i++)
+        for (int t = 0; t < C::kTiles; t++) {
+            if (t < t0 || t >= t0 + C::kRedTiles)
+                continue;
+            const int i = t / TN, j = t % TN;
 #pragma unroll
-            for (int j = 0; j < TN; j++) {
-                if (wk > 0) {
+            for (int r = 0; r < 4; r++)
+                red[((wave * C::kRedTiles + (t - t0)) * 4 + r) * 64 + lane] = acc[i][j][r];
+        }
+        __syncthreads();
+        for (int tt = wave; tt < C::kRedTiles && t0 + tt < C::kTiles; tt += WAVES) {
+            const int t = t0 + tt;
+            const int i = t / TN, j = t % TN;
+            const int64_t col = col0 + j * 16 + j16;
 #pragma unroll
-                    for (int r = 0; r < 16; r++)
-                        red[((grp * (WK - 1) + wk - 1) * 16 + r) * 64 + lane] = acc[i][j][r];
-                }
-                __syncthreads();
-                if (wk == 0) {
-                    for (int w = 1; w < WK; w++)
+            for (int r = 0; r < 4; r++) {
+                float v = red[((0 * C::kRedTiles + tt) * 4 + r) * 64 + lane];
 #pragma unroll
-                        for (int r = 0; r < 16; r++)
-                            acc[i][j][r] += red[((grp * (WK - 1) + w - 1) * 16 + r) * 64 + lane];
-                }
-                __syncthreads();
-            }
-        if (wk > 0)
-            return;
-    }
-
-#pragma unroll
-    for (int i = 0; i < TM; i++) {
-        if (vrows[i] <= 0)
-            continue;
-#pragma unroll
-        for (int j = 0; j < TN; j++) {
-            const int64_t col = col0 + (wn * TN + j) * 32 + rr;
-#pragma unroll
-            for (int r = 0; r < 16; r++) {
-                const int rl = 8 * (r / 4) + 4 * g + (r % 4);
-                if (rl < vrows[i]) {
-                    const int64_t row = row0 + (wm * TM + i) * 32 + rl;
-                    p.y[row * p.ldy + col] = acc[i][j][r];
-                }
+                for (int w = 1; w < WAVES; w++)
+                    v += red[((w * C::kRedTiles + tt) * 4 + r) * 64 + lane];
+                const int rl = 4 * g + r;
+                if (rl < vrows[i])
+                    p.y[(row0 + i * 16 + rl) * p.ldy + col] = v * unscale;
             }
         }
+        __syncthreads();
     }
 }
 
@@ -503,46 +485,96 @@ hipError_t launch_cfg(const GemmProblem &p, int tiles_m, int tiles_n, int tm0, i
     return hipGetLastError();
 }
 
-// Tile shapes.  Large M: 64x64 workgroup tiles, one 32x32 tile per wave.
-// Small M (<= 32): one 32-row tile, 64 columns, K split over two waves.
-template <int BITS> using CfgLarge = Cfg<BITS, 64, 64, 8, 2, 2, 1>;
-template <int BITS> using CfgSmall = Cfg<BITS, 32, 64, 8, 1, 2, 2>;
+template <class C>
+hipError_t launch_dense_cfg(const GemmProblem &p, hipStream_t stream)
+{
+    const int tm = (int)((p.rows + C::BM - 1) / C::BM), tn = (int)(p.n / C::BN);
+    return launch_cfg<C, kGemm>(p, tm, tn, 0, 0, (int64_t)tm * tn, stream);
+}
+
+// Dense tile shapes (rows x columns), KC = 8 blocks per stage (2 per wave).
+// Two workgroups per CU.
+template <int BITS> struct Tiles {
+    static constexpr int KC = 8;
+    // 8-bit codes double the A staging registers: the widest tile stages 4
+    // blocks at a time so that it still fits two workgroups per CU
+    using T64x80 = Cfg<BITS, 64, 80, BITS == 8 ? 4 : KC>;
+    using T64x64 = Cfg<BITS, 64, 64, KC>;
+    using T32x128 = Cfg<BITS, 32, 128, KC>;
+    using T16x64 = Cfg<BITS, 16, 64, KC>;
+    using T16x32 = Cfg<BITS, 16, 32, KC>;
+    using T64x32 = Cfg<BITS, 64, 32, KC>;
+    using T32x64 = Cfg<BITS, 32, 64, KC>;
+};
+
+constexpr int kCUs = 256;
+
+// Pick the shape with the smallest estimated time: rounds of 2 workgroups per
+// CU times the per-tile cost, where the cost counts the epilogue (2 per sum)
+// plus operand unpacking (3 per row tile, 5 per column tile, per 16x16x32).
+inline double est(int64_t m, int64_t n, int bm, int bn)
+{
+    if (n % bn != 0)
+        return 1e300;
+    const int64_t tiles = ((m + bm - 1) / bm) * (n / bn);
+    const int64_t slots = 2 * kCUs;
+    const double rounds = (double)((tiles + slots - 1) / slots);
+    const double tm = bm / 16.0, tn = bn / 16.0;
+    const double cost = 8.0 * tm * tn + 3.0 * tm + 5.0 * tn;
+    return rounds * cost;
+}
 
 template <int BITS>
 hipError_t launch_dense_bits(const GemmProblem &p, hipStream_t stream)
 {
-    if (p.rows <= 32) {
-        using C = CfgSmall<BITS>;
-        const int tm = (int)((p.rows + C::BM - 1) / C::BM), tn = (int)(p.n / C::BN);
-        if (p.n % C::BN == 0)
-            return launch_cfg<C, kGemm>(p, tm, tn, 0, 0, (int64_t)tm * tn, stream);
+    using T = Tiles<BITS>;
+    const int64_t m = p.rows, n = p.n;
+    if (m <= 16) {
+        if (est(m, n, 16, 64) <= est(m, n, 16, 32))
+            return launch_dense_cfg<typename T::T16x64>(p, stream);
+        return launch_dense_cfg<typename T::T16x32>(p, stream);
     }
-    using C = CfgLarge<BITS>;
-    if (p.n % C::BN == 0) {
-        const int tm = (int)((p.rows + C::BM - 1) / C::BM), tn = (int)(p.n / C::BN);
-        return launch_cfg<C, kGemm>(p, tm, tn, 0, 0, (int64_t)tm * tn, stream);
+    struct Cand { int bm, bn, id; };
+    const Cand cands[] = {{64, 80, 0}, {64, 64, 1}, {32, 128, 2}, {32, 64, 3}, {64, 32, 4}};
+    int best = 4;
+    double best_t = est(m, n, 64, 32);
+    for (const Cand &c : cands) {
+        const double t = est(m, n, c.bm, c.bn);
+        if (t < best_t) {
+            best_t = t;
+            best = c.id;
+        }
     }
-    using C32 = Cfg<BITS, 64, 32, 8, 2, 1, 1>; // N a multiple of 32 only
-    const int tm = (int)((p.rows + C32::BM - 1) / C32::BM), tn = (int)(p.n / C32::BN);
-    return launch_cfg<C32, kGemm>(p, tm, tn, 0, 0, (int64_t)tm * tn, stream);
+    switch (best) {
+    case 0: return launch_dense_cfg<typename T::T64x80>(p, stream);
+    case 1: return launch_dense_cfg<typename T::T64x64>(p, stream);
+    case 2: return launch_dense_cfg<typename T::T32x128>(p, stream);
+    case 3: return launch_dense_cfg<typename T::T32x64>(p, stream);
+    default: return launch_dense_cfg<typename T::T64x32>(p, stream);
+    }
 }
 
 template <int BITS>
 hipError_t launch_grouped_bits(const GemmProblem &p, hipStream_t stream)
 {
-    using C = Cfg<BITS, 64, 32, 8, 2, 1, 1>;
-    const int tn = (int)(p.n / C::BN);
+    using C = Cfg<BITS, 32, 64, Tiles<BITS>::KC>;
+    using C32 = Cfg<BITS, 32, 32, Tiles<BITS>::KC>;
     // every expert needs ceil(rows_e / BM) slots: bounded by both of these
     int64_t slots = (p.rows + p.experts * (C::BM - 1)) / C::BM;
     if (slots > p.rows)
         slots = p.rows;
-    return launch_cfg<C, kGrouped>(p, 0, tn, 0, 0, slots * tn, stream);
+    if (p.n % C::BN == 0) {
+        const int tn = (int)(p.n / C::BN);
+        return launch_cfg<C, kGrouped>(p, 0, tn, 0, 0, slots * tn, stream);
+    }
+    const int tn = (int)(p.n / C32::BN);
+    return launch_cfg<C32, kGrouped>(p, 0, tn, 0, 0, slots * tn, stream);
 }
 
 template <int BITS>
 hipError_t launch_sums_bits(const GemmProblem &p, hipStream_t stream)
 {
-    using C = Cfg<BITS, 64, 32, 8, 2, 1, 1>;
+    using C = Cfg<BITS, 32, 32, Tiles<BITS>::KC>;
     const int tm0 = (int)(p.m0 / C::BM), tm1 = (int)((p.m1 + C::BM - 1) / C::BM);
     const int tn0 = (int)(p.n0 / C::BN), tn1 = (int)((p.n1 + C::BN - 1) / C::BN);
     const int tm = tm1 - tm0, tn = tn1 - tn0;

@@ -37,6 +37,8 @@
  *   - device calls are asynchronous on `stream` (a hipStream_t; NULL = the
  *     null stream); execution faults surface at the caller's synchronisation;
  *   - the caller owns every buffer; device pointers must be 16-byte aligned;
+ *     when the row count is 0, activation, code, scale and output pointers
+ *     may be NULL (nothing is read or written);
  *   - K (input channels) is a multiple of 32, N (output channels) a multiple
  *     of 32; M (tokens) may be 0 (the call is then a no-op after its checks);
  *   - inputs are finite; NaN or Inf input gives unspecified codes.

@@ -113,6 +113,15 @@ def test_gemm_errors(kwargs, status):
     assert gemm(**kwargs) == status
 
 
+def test_zero_rows_accept_null_buffers():
+    """Empty tensors may carry NULL pointers; with no rows nothing is touched."""
+    if os.path.exists("/dev/kfd"):
+        pytest.skip("host has a GPU driver")
+    assert q(x=NUL, codes=NUL, scales=NUL, m=0) == DEVICE
+    assert gemm(codes=NUL, scales=NUL, y=NUL, m=0) == DEVICE
+    assert gemm(codes=NUL, m=1) == NULL
+
+
 def test_gemm_null_desc():
     lib = bb.lib()
     assert lib.w4a4_gemm(P, P2, 4, 4, None, P, P2, 64, NUL) == NULL
