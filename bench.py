@@ -2,21 +2,33 @@
 """Benchmark of the Hadamard-rotated W4A4 prompt GEMM on one MI355X.
 
 A step is one pass of the route over one batch: quantize_act_h32 (FWHT-32 +
-4-bit quantization of the activations) then w4a4_gemm, on the dense
-attention projection at 512 prompt tokens (M=512, K=5120, N=5120, bf16
-activations).  Inputs are resident in HBM before the timed region; each step
-uses a different copy of the weights and activations, cycling through enough
-copies (>= 512 MB) that the 256 MB last-level cache cannot hold them.
+4-bit quantization of the activations) then w4a4_gemm, by default on the
+dense attention projection at 512 prompt tokens (M=512, K=5120, N=5120, bf16
+activations, rotated Q4_0 weights).  The weight image is packed once, outside
+the timed region (it is the offline step).  Inputs are resident in HBM before
+the timed region; each step uses a different copy of the weights and
+activations, cycling through enough copies (>= 512 MB) that the 256 MB
+last-level cache cannot hold them.
 
 Prints ONE JSON line.  `value` is prompt tokens per second of the step.  The
-`roofline` object covers the GEMM kernel (the dominant kernel): its average
+`roofline` object covers the GEMM kernel (the dominant kernel).  Its average
 duration is measured with HIP events recorded on the launch stream around
-every GEMM in the timed region.  `cpu_baseline` times the CPU oracle on the
-same workload (test infrastructure, not the product path).
+every GEMM in the timed region.  The kernel is bound by its fp32 VALU
+epilogue (two VALU operations per output element and 32-block), so the
+roofline is taken against the VALU issue rate; the int8 matrix-core view
+(effective TOPS against the dense int8 peak) is reported beside it.
+`traffic` comes from the committed rocprofv3 counter summary for this kernel
+and workload, and is null if the kernel source changed since it was taken.
+`cpu_baseline` times the CPU oracle on the same workload (test
+infrastructure, not the product path).
+
+`--copy-calibration BYTES` instead runs a plain device copy of that size
+(for scaling the FETCH_SIZE / WRITE_SIZE counters) and prints nothing else.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -30,19 +42,21 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 # MI355X published peaks
-PEAK_INT8_OPS = 5.0e15          # dense int8 MFMA, ops/s
-PEAK_HBM = 8.0e12               # bytes/s
-# fp32 VALU issue rate with packed fp32 instructions disabled:
-# 256 CU x 4 SIMD x 16 lanes x 2.4 GHz = 39.3e12 lane-ops/s
-PEAK_VALU_OPS = 256 * 4 * 16 * 2.4e9
+PEAK_INT8_OPS = 5.0e15                    # dense int8 matrix ops/s
+PEAK_HBM = 8.0e12                         # bytes/s
+# fp32 VALU issue rate with packed fp32 instructions unused:
+# 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz
+PEAK_VALU_OPS = 256 * 4 * 16 * 2.4e9      # 39.3e12 lane-operations/s
 
 WORKLOADS = {
-    "attn512": dict(m=512, k=5120, n=5120, key="x"),
-    "long1024": dict(m=1024, k=5120, n=17408, key="x"),
-    "m16_gate": dict(m=16, k=5120, n=17408, key="x"),
-    "m16_down": dict(m=16, k=17408, n=5120, key="x"),
-    "m16_attn": dict(m=16, k=5120, n=5120, key="x"),
+    "attn512": dict(m=512, k=5120, n=5120),
+    "long1024": dict(m=1024, k=5120, n=17408),
+    "m16_gate": dict(m=16, k=5120, n=17408),
+    "m16_down": dict(m=16, k=17408, n=5120),
+    "m16_attn": dict(m=16, k=5120, n=5120),
 }
+GEMM_SRC = os.path.join(ROOT, "bit_prefill_gemm_amd", "csrc", "gemm.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_traffic.json")
 
 
 def parse():
@@ -56,6 +70,7 @@ def parse():
                     help="total bytes of distinct input copies cycled through")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-calibration", type=float, default=0.0)
     return ap.parse_args()
 
 
@@ -64,9 +79,27 @@ def gemm_bytes(m, k, n, bits):
     return n * k * 18 // 32 + m * k * bits // 8 + m * (k // 32) * 4 + m * n * 4
 
 
-def cpu_baseline(data, wl, bits, seconds):
+def source_hash():
+    return hashlib.sha256(open(GEMM_SRC, "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic(workload, bits):
+    """HBM bytes per GEMM launch from the committed counter summary, if still current."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if rec.get("gemm_source_sha256_16") != source_hash():
+        return None
+    e = rec.get("workloads", {}).get("%s/%d" % (workload, bits))
+    if not e:
+        return None
+    return e["fetch_bytes"] + e["write_bytes"]
+
+
+def cpu_baseline(data, wl, name, bits, seconds):
     import oracle
-    x = data[wl["key"]]
+    x = data["x"]
     m, k, n = wl["m"], wl["k"], wl["n"]
     w, dw = oracle.q4_0_decode(data["w"], k)
     reps, t0 = 0, time.perf_counter()
@@ -79,15 +112,18 @@ def cpu_baseline(data, wl, bits, seconds):
             break
     return {"value": reps * m / el, "unit": "tokens/s", "cores": oracle.num_threads(),
             "kind": "oracle",
-            "sample": "whole %s workload (quantize %dx%d + %dx%dx%d GEMM, fp64 output), "
-                      "%d repetition(s) in %.1f s" % (wl_name_of(wl), m, k, m, k, n, reps, el)}
+            "sample": "whole %s workload (quantize %dx%d, then %dx%dx%d GEMM with fp64 "
+                      "output), %d repetition(s) in %.1f s" % (name, m, k, m, k, n, reps, el)}
 
 
-def wl_name_of(wl):
-    for name, v in WORKLOADS.items():
-        if v is wl:
-            return name
-    return "?"
+def copy_calibration(nbytes):
+    import torch
+    n = int(nbytes) // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
 
 
 def main():
@@ -105,15 +141,17 @@ def main():
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     bb.lib()
     wl = WORKLOADS[args.workload]
     m, k, n, bits = wl["m"], wl["k"], wl["n"], args.bits
     data = synth.make(args.workload)
-    x_host = data[wl["key"]]
     W0 = bb.rotate_pack_weights(data["w"], bb.SRC_Q4_0_ROTATED, n, k)
 
     dev = torch.device("cuda:0")
-    x0 = torch.from_numpy(x_host.view(np.int16)).to(dev).view(torch.bfloat16)
+    x0 = torch.from_numpy(data["x"].view(np.int16)).to(dev).view(torch.bfloat16)
     img0 = torch.from_numpy(W0.image).to(dev)
     per_copy = img0.numel() + x0.numel() * 2
     copies = max(1, int(math.ceil(args.cold_bytes / per_copy)))
@@ -127,18 +165,20 @@ def main():
 
     def step(i, ev=None):
         j = i % copies
-        bb.quantize_act_h32(xs[j], bits, codes=codes, scales=scales, stream=stream)
         if ev is not None:
             ev[0].record(stream)
-        bb.w4a4_gemm(codes, scales, bits, Ws[j], y=y, stream=stream)
+        bb.quantize_act_h32(xs[j], bits, codes=codes, scales=scales, stream=stream)
         if ev is not None:
             ev[1].record(stream)
+        bb.w4a4_gemm(codes, scales, bits, Ws[j], y=y, stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
 
     with torch.cuda.stream(stream):
         for i in range(args.warmup):
             step(i)
         torch.cuda.synchronize()
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+        evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3))
                for _ in range(args.steps)]
         t0 = time.perf_counter()
         for i in range(args.steps):
@@ -147,13 +187,14 @@ def main():
         t1 = time.perf_counter()
 
     ms_per_step = (t1 - t0) * 1e3 / args.steps
-    gemm_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    quant_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    gemm_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
     gemm_s = gemm_ms * 1e-3
     ops = 2.0 * m * n * k
     eff_tops = ops / gemm_s / 1e12
-    # the fp32 epilogue: two VALU operations per (m, n, 32-block)
-    epi_ops = 2.0 * m * n * (k // 32)
+    epi_ops = 2.0 * m * n * (k // 32)     # algorithmic fp32 VALU lane-operations
     gbytes = gemm_bytes(m, k, n, bits)
+    traffic = measured_traffic(args.workload, bits)
 
     out = {
         "metric": "prompt tokens/s + effective TOPS (% int8 MFMA peak) for rotated W4A4 GEMM, M=512",
@@ -166,24 +207,29 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "i8" if bits == 8 else "i4 (i8 MFMA operands, fp32 block-scale epilogue)",
+        "dtype": "i8" if bits == 8 else "i4",
         "data": "synthetic",
         "config": {"workload": "%s: M=%d K=%d N=%d, bf16 activations, rotated Q4_0 weights, "
                                "%d-bit activation codes" % (args.workload, m, k, n, bits),
                    "m": m, "k": k, "n": n, "act_bits": bits, "cold_copies": copies},
-        "roofline": {"bound": "mfma", "achieved": eff_tops, "peak": PEAK_INT8_OPS / 1e12,
-                     "unit": "TOP/s (int8)", "frac": eff_tops / (PEAK_INT8_OPS / 1e12),
-                     "traffic": None},
-        "gemm_us": gemm_ms * 1e3,
-        "step_us": ms_per_step * 1e3,
+        "roofline": {"bound": "alu", "achieved": epi_ops / gemm_s / 1e12,
+                     "peak": PEAK_VALU_OPS / 1e12, "unit": "T fp32 VALU lane-op/s",
+                     "frac": epi_ops / gemm_s / PEAK_VALU_OPS, "traffic": traffic,
+                     "kernel": "w4a4_gemm"},
+        "int8_mfma": {"achieved": eff_tops, "peak": PEAK_INT8_OPS / 1e12, "unit": "TOP/s",
+                      "frac": eff_tops / (PEAK_INT8_OPS / 1e12)},
         "eff_TOPS": eff_tops,
         "pct_int8_peak": 100.0 * eff_tops / (PEAK_INT8_OPS / 1e12),
+        "gemm_us": gemm_ms * 1e3,
+        "quant_us": quant_ms * 1e3,
+        "step_us": ms_per_step * 1e3,
         "gemm_hbm_GBps": gbytes / gemm_s / 1e9,
         "pct_hbm": 100.0 * gbytes / gemm_s / PEAK_HBM,
-        "epilogue_valu_frac": epi_ops / gemm_s / PEAK_VALU_OPS,
+        "gemm_algorithmic_bytes": gbytes,
+        "gemm_source_sha256_16": source_hash(),
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(data, wl, bits, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(data, wl, args.workload, bits, args.cpu_seconds)
     print(json.dumps(out))
 
 

@@ -33,6 +33,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "internal.h"
 
 namespace bpg {
@@ -46,12 +48,16 @@ constexpr float kMagic = 12582912.0f;
 
 enum Mode { kGemm = 0, kGrouped = 1, kSums = 2 };
 
-template <int BITS_, int BM_, int BN_, int KC_>
+// Wave layout: WM x WN x WK waves; wave (wm, wn, wk) owns the TM x TN
+// 16x16 tiles at row tile wm*TM and column tile wn*TN of the workgroup tile
+// and every WK-th block of a stage (the K split).
+template <int BITS_, int TM_, int TN_, int WM_, int WN_, int WK_, int KC_>
 struct Cfg {
-    static constexpr int BITS = BITS_, BM = BM_, BN = BN_, KC = KC_;
-    static constexpr int kWaves = 4;
+    static constexpr int BITS = BITS_, TM = TM_, TN = TN_, KC = KC_;
+    static constexpr int WM = WM_, WN = WN_, WK = WK_;
+    static constexpr int kWaves = WM * WN * WK;
     static constexpr int kThreads = 64 * kWaves;
-    static constexpr int TM = BM / 16, TN = BN / 16;
+    static constexpr int BM = 16 * TM * WM, BN = 16 * TN * WN;
     static constexpr int kAB = BITS == 4 ? 16 : 32;   // code bytes per (row, block)
     static constexpr int kShift = BITS == 4 ? 8 : 4;  // log2 of the operand widening
     // one stage in LDS: A codes [KC][BM][kAB], W codes [KC][BN][16],
@@ -61,9 +67,9 @@ struct Cfg {
     static constexpr int kLdsDa = KC * BM * 4;
     static constexpr int kLdsDw = KC * BN * 8;
     static constexpr int kStage = kLdsA + kLdsW + kLdsDa + kLdsDw;
-    static constexpr int kTiles = TM * TN;
+    static constexpr int kTiles = TM * TN; // per wave
     // final reduction: every wave parks the partial sums of up to kRedTiles
-    // tiles at a time ([wave][tile][4 regs][64 lanes] fp32)
+    // of its tiles at a time ([group][wk][tile][4 regs][64 lanes] fp32)
     static constexpr int kRedTiles = kTiles < 16 ? kTiles : 16;
     static constexpr int kLdsRed = kWaves * kRedTiles * 4 * 64 * 4;
     static constexpr int kLds = 2 * kStage > kLdsRed ? 2 * kStage : kLdsRed;
@@ -74,7 +80,8 @@ struct Cfg {
     static constexpr int kPtW = (kChW + kThreads - 1) / kThreads;
     static constexpr int kPtDa = (BM * KC + kThreads - 1) / kThreads;
     static constexpr int kPtDw = (BN * KC + kThreads - 1) / kThreads;
-    static_assert(BM % 16 == 0 && BN % 16 == 0 && KC % kWaves == 0, "tiling");
+    static constexpr int kOcc = kThreads >= 512 ? 1 : 2; // workgroups per CU aimed at
+    static_assert(KC % WK == 0, "K split");
     static_assert(kLds <= 160 * 1024, "LDS budget");
 };
 
@@ -88,7 +95,13 @@ __device__ __forceinline__ long widen_act4(uint32_t d)
 }
 
 // Q4_0 nibbles u -> top bit flipped (u XOR 8 is u-8 in two's complement) -> 16*(u-8).
-__device__ __forceinline__ long widen_q4_0(uint32_t d) { return widen_act4(d ^ 0x88888888u); }
+// Each half is one shift at most plus one three-input bit operation.
+__device__ __forceinline__ long widen_q4_0(uint32_t d)
+{
+    const uint32_t lo = ((d << 4) ^ 0x80808080u) & 0xF0F0F0F0u;
+    const uint32_t hi = (d ^ 0x88888888u) & 0xF0F0F0F0u;
+    return (long)(((uint64_t)hi << 32) | lo);
+}
 
 __device__ __forceinline__ float half_bits_to_float(uint16_t h)
 {
@@ -159,11 +172,11 @@ __device__ bool grouped_slot(const int32_t *__restrict__ off, int64_t experts, i
 }
 
 template <class C, int MODE>
-__global__ __launch_bounds__(C::kThreads, 2) void w4a4_kernel(GemmProblem p, int tiles_m,
+__global__ __launch_bounds__(C::kThreads, C::kOcc) void w4a4_kernel(GemmProblem p, int tiles_m,
                                                               int tiles_n, int tm0, int tn0)
 {
     constexpr int BM = C::BM, BN = C::BN, KC = C::KC, TM = C::TM, TN = C::TN;
-    constexpr int NT = C::kThreads, kAB = C::kAB, WAVES = C::kWaves;
+    constexpr int NT = C::kThreads, kAB = C::kAB, WK = C::WK;
     __shared__ __attribute__((aligned(16))) uint8_t lds[C::kLds];
 
     const int tid = threadIdx.x;
@@ -171,6 +184,10 @@ __global__ __launch_bounds__(C::kThreads, 2) void w4a4_kernel(GemmProblem p, int
     const int j16 = lane & 15; // row (A operand) / column (B operand, output) in a 16-tile
     const int g = lane >> 4;   // K group of the operands; output rows 4g..4g+3
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wk = wave % C::WK;
+    const int wn = (wave / C::WK) % C::WN;
+    const int wm = wave / (C::WK * C::WN);
+    const int grp = wm * C::WN + wn; // waves of one group share tiles, split K
 
     const int64_t B = p.k / 32;
     const int64_t ntiles32 = p.n / 32;
@@ -258,61 +275,68 @@ __global__ __launch_bounds__(C::kThreads, 2) void w4a4_kernel(GemmProblem p, int
     float rda[C::kPtDa];
     uint16_t rdw[C::kPtDw];
 
-    // Loads of blocks past K (only in a last, partial stage) are skipped.
-    auto load_stage = [&](int64_t kb0) {
-        const int kv = (int)(B - kb0 < KC ? B - kb0 : KC);
+    // Chunk i of a thread exists for every thread when (i+1)*NT <= count;
+    // only the last chunk of a region can exist for some threads only.
+#define BPG_CHUNK_OK(i, count) ((((i) + 1) * NT <= (count)) || (tid + (i) * NT < (count)))
+    // Full stages read every chunk; the last, partial stage skips blocks past K.
+    auto load_stage = [&](int64_t kb0, auto full_tag) {
+        constexpr bool full = decltype(full_tag)::value;
+        const int kv = full ? KC : (int)(B - kb0);
         const uint8_t *ab = a_base0 + kb0 * kAB;
         const uint8_t *wb = w_base0 + kb0 * 512;
         const float *dab = da_base0 + kb0;
         const uint16_t *dwb = dw_base0 + kb0 * 32;
 #pragma unroll
         for (int i = 0; i < C::kPtA; i++)
-            ra[i] = kca[i] < kv ? *reinterpret_cast<const uint4 *>(ab + oa[i]) : make_uint4(0, 0, 0, 0);
+            ra[i] = (BPG_CHUNK_OK(i, C::kChA) && (full || kca[i] < kv))
+                        ? *reinterpret_cast<const uint4 *>(ab + oa[i]) : make_uint4(0, 0, 0, 0);
 #pragma unroll
         for (int i = 0; i < C::kPtW; i++)
-            rw[i] = kcw[i] < kv ? *reinterpret_cast<const uint4 *>(wb + ow[i]) : make_uint4(0, 0, 0, 0);
+            rw[i] = (BPG_CHUNK_OK(i, C::kChW) && (full || kcw[i] < kv))
+                        ? *reinterpret_cast<const uint4 *>(wb + ow[i]) : make_uint4(0, 0, 0, 0);
         if (MODE != kSums) { // block sums never read scales
 #pragma unroll
             for (int i = 0; i < C::kPtDa; i++)
-                rda[i] = kcda[i] < kv ? dab[oda[i]] : 0.0f;
+                rda[i] = (BPG_CHUNK_OK(i, BM * KC) && (full || kcda[i] < kv)) ? dab[oda[i]] : 0.0f;
 #pragma unroll
             for (int i = 0; i < C::kPtDw; i++)
-                rdw[i] = kcdw[i] < kv ? dwb[odw[i]] : (uint16_t)0;
+                rdw[i] = (BPG_CHUNK_OK(i, BN * KC) && (full || kcdw[i] < kv)) ? dwb[odw[i]]
+                                                                               : (uint16_t)0;
         }
     };
 
-    auto store_stage = [&](int buf) {
-        uint8_t *A = lds + buf * C::kStage;
+    auto store_stage = [&](uint8_t *A) {
         uint8_t *W = A + C::kLdsA;
         float *Da = reinterpret_cast<float *>(W + C::kLdsW);
         float2 *Dw = reinterpret_cast<float2 *>(W + C::kLdsW + C::kLdsDa);
 #pragma unroll
         for (int i = 0; i < C::kPtA; i++)
-            if (kca[i] < KC)
+            if (BPG_CHUNK_OK(i, C::kChA))
                 *reinterpret_cast<uint4 *>(A + la[i]) = ra[i];
 #pragma unroll
         for (int i = 0; i < C::kPtW; i++)
-            if (kcw[i] < KC)
+            if (BPG_CHUNK_OK(i, C::kChW))
                 *reinterpret_cast<uint4 *>(W + lw[i]) = rw[i];
         if (MODE != kSums) {
 #pragma unroll
             for (int i = 0; i < C::kPtDa; i++)
-                if (kcda[i] < KC)
+                if (BPG_CHUNK_OK(i, BM * KC))
                     Da[lda_[i]] = rda[i];
 #pragma unroll
             for (int i = 0; i < C::kPtDw; i++)
-                if (kcdw[i] < KC) {
+                if (BPG_CHUNK_OK(i, BN * KC)) {
                     const float dw = half_bits_to_float(rdw[i]);
                     Dw[ldw_[i]] = make_float2(dw, -kMagic * dw);
                 }
         }
     };
+#undef BPG_CHUNK_OK
 
     // 16-row tiles of the workgroup tile that hold data (uniform per workgroup)
     int vrows[TM];
 #pragma unroll
     for (int i = 0; i < TM; i++) {
-        const int64_t v = row_end - (row0 + (int64_t)i * 16);
+        const int64_t v = row_end - (row0 + (int64_t)(wm * TM + i) * 16);
         vrows[i] = v < 0 ? 0 : (v > 16 ? 16 : (int)v);
     }
 
@@ -331,25 +355,23 @@ __global__ __launch_bounds__(C::kThreads, 2) void w4a4_kernel(GemmProblem p, int
         magic[r] = kMagicBits;
 
     const int64_t nstages = (B + KC - 1) / KC;
-    load_stage(0);
-    store_stage(0);
+    if (KC <= B)
+        load_stage(0, std::true_type{});
+    else
+        load_stage(0, std::false_type{});
+    store_stage(lds);
     __syncthreads();
 
-    for (int64_t s = 0; s < nstages; s++) {
-        const int buf = (int)(s & 1);
-        const int64_t kb0 = s * KC;
-        if (s + 1 < nstages)
-            load_stage(kb0 + KC);
-
-        const uint8_t *A = lds + buf * C::kStage;
+    // One stage of arithmetic on the operands held in buffer A.
+    auto compute_stage = [&](const uint8_t *A, int64_t kb0) {
         const uint8_t *W = A + C::kLdsA;
         const float *Da = reinterpret_cast<const float *>(W + C::kLdsW);
         const float2 *Dw = reinterpret_cast<const float2 *>(W + C::kLdsW + C::kLdsDa);
         const int64_t kvalid = B - kb0; // >= 1
 
 #pragma unroll
-        for (int kk = 0; kk < KC / WAVES; kk++) {
-            const int kc = kk * WAVES + wave;
+        for (int kk = 0; kk < KC / WK; kk++) {
+            const int kc = kk * WK + wk;
             if (kc >= kvalid)
                 break;
             // A operands: row j16 of each 16-row tile, K group g
@@ -360,9 +382,9 @@ __global__ __launch_bounds__(C::kThreads, 2) void w4a4_kernel(GemmProblem p, int
 #pragma unroll
             for (int i = 0; i < TM; i++) {
                 if (kAB == 16) {
-                    a[i] = widen_act4(*reinterpret_cast<const uint32_t *>(A + (kc * BM + i * 16 + sw16) * 16 + 4 * g));
+                    a[i] = widen_act4(*reinterpret_cast<const uint32_t *>(A + (kc * BM + (wm * TM + i) * 16 + sw16) * 16 + 4 * g));
                 } else {
-                    const int srow = i * 16 + sw16;
+                    const int srow = (wm * TM + i) * 16 + sw16;
                     const int sw = (srow >> 3) & 1;
                     const uint32_t lo = *reinterpret_cast<const uint32_t *>(A + (kc * BM + srow) * 32 + (sw * 16) + 4 * g);
                     const uint32_t hi = *reinterpret_cast<const uint32_t *>(A + (kc * BM + srow) * 32 + ((sw ^ 1) * 16) + 4 * g);
@@ -373,14 +395,14 @@ __global__ __launch_bounds__(C::kThreads, 2) void w4a4_kernel(GemmProblem p, int
             if (MODE == kSums) {
 #pragma unroll
                 for (int j = 0; j < TN; j++) {
-                    const long b = widen_q4_0(*reinterpret_cast<const uint32_t *>(W + (kc * BN + j * 16 + swc) * 16 + 4 * g));
-                    const int64_t col = col0 + j * 16 + j16;
+                    const long b = widen_q4_0(*reinterpret_cast<const uint32_t *>(W + (kc * BN + (wn * TN + j) * 16 + swc) * 16 + 4 * g));
+                    const int64_t col = col0 + (wn * TN + j) * 16 + j16;
 #pragma unroll
                     for (int i = 0; i < TM; i++) {
                         const v4i D = __builtin_amdgcn_mfma_i32_16x16x32_i8(a[i], b, magic, 0, 0, 0);
 #pragma unroll
                         for (int r = 0; r < 4; r++) {
-                            const int64_t row = row0 + i * 16 + 4 * g + r;
+                            const int64_t row = row0 + (wm * TM + i) * 16 + 4 * g + r;
                             if (row >= p.m0 && row < p.m1 && col >= p.n0 && col < p.n1)
                                 p.sums[((row - p.m0) * (p.n1 - p.n0) + (col - p.n0)) * B + kb0 + kc] =
                                     (D[r] - kMagicBits) >> C::kShift;
@@ -391,7 +413,7 @@ __global__ __launch_bounds__(C::kThreads, 2) void w4a4_kernel(GemmProblem p, int
                 float4 da[TM];
 #pragma unroll
                 for (int i = 0; i < TM; i++)
-                    da[i] = *reinterpret_cast<const float4 *>(Da + kc * BM + i * 16 + 4 * g);
+                    da[i] = *reinterpret_cast<const float4 *>(Da + kc * BM + (wm * TM + i) * 16 + 4 * g);
                 // Software pipeline over the column tiles: the matrix
                 // instructions of tile j are issued before the epilogue of
                 // tile j-1, so their latency hides behind VALU work.  Padded
@@ -403,8 +425,8 @@ __global__ __launch_bounds__(C::kThreads, 2) void w4a4_kernel(GemmProblem p, int
                     v4i Dc[TM];
                     float2 dwc = make_float2(0.0f, 0.0f);
                     if (j < TN) {
-                        const long b = widen_q4_0(*reinterpret_cast<const uint32_t *>(W + (kc * BN + j * 16 + swc) * 16 + 4 * g));
-                        dwc = Dw[kc * BN + j * 16 + j16];
+                        const long b = widen_q4_0(*reinterpret_cast<const uint32_t *>(W + (kc * BN + (wn * TN + j) * 16 + swc) * 16 + 4 * g));
+                        dwc = Dw[kc * BN + (wn * TN + j) * 16 + j16];
 #pragma unroll
                         for (int i = 0; i < TM; i++)
                             Dc[i] = __builtin_amdgcn_mfma_i32_16x16x32_i8(a[i], b, magic, 0, 0, 0);
@@ -430,42 +452,64 @@ __global__ __launch_bounds__(C::kThreads, 2) void w4a4_kernel(GemmProblem p, int
             }
         }
 
-        if (s + 1 < nstages)
-            store_stage(buf ^ 1);
-        __syncthreads();
+    };
+
+    // Stages alternate between the two buffers; the loop is unrolled by two
+    // so that every LDS address carries its buffer offset as an immediate.
+    for (int64_t s = 0; s < nstages; s += 2) {
+#pragma unroll
+        for (int half = 0; half < 2; half++) {
+            const int64_t st = s + half;
+            if (st < nstages) {
+                const int64_t kb0 = st * KC;
+                const bool more = st + 1 < nstages;
+                if (more) {
+                    if (kb0 + 2 * KC <= B)
+                        load_stage(kb0 + KC, std::true_type{});
+                    else
+                        load_stage(kb0 + KC, std::false_type{});
+                }
+                compute_stage(lds + half * C::kStage, kb0);
+                if (more)
+                    store_stage(lds + (half ^ 1) * C::kStage);
+                __syncthreads();
+            }
+        }
     }
 
     if (MODE == kSums)
         return;
 
-    // ---- fixed-order sum of the four waves' partials; each wave stores a
-    //      quarter of the tiles.  The widening factor 2^kShift is removed here.
+    // ---- fixed-order sum of the K-split partials of each wave group (wk = 0,
+    //      1, ... in order); the waves of a group share the stores.  The
+    //      widening factor 2^kShift is removed here.
     const float unscale = 1.0f / (float)(1 << C::kShift);
     float *red = reinterpret_cast<float *>(lds);
-    for (int t0 = 0; t0 < C::kTiles; t0 += C::kRedTiles) {
+    constexpr int R = C::kRedTiles;
+    for (int t0 = 0; t0 < C::kTiles; t0 += R) {
 #pragma unroll
         for (int t = 0; t < C::kTiles; t++) {
-            if (t < t0 || t >= t0 + C::kRedTiles)
+            if (t < t0 || t >= t0 + R)
                 continue;
             const int i = t / TN, j = t % TN;
 #pragma unroll
             for (int r = 0; r < 4; r++)
-                red[((wave * C::kRedTiles + (t - t0)) * 4 + r) * 64 + lane] = acc[i][j][r];
+                red[(((grp * WK + wk) * R + (t - t0)) * 4 + r) * 64 + lane] = acc[i][j][r];
         }
         __syncthreads();
-        for (int tt = wave; tt < C::kRedTiles && t0 + tt < C::kTiles; tt += WAVES) {
+        for (int tt = wk; tt < R && t0 + tt < C::kTiles; tt += WK) {
             const int t = t0 + tt;
             const int i = t / TN, j = t % TN;
-            const int64_t col = col0 + j * 16 + j16;
+            const int64_t col = col0 + (wn * TN + j) * 16 + j16;
 #pragma unroll
             for (int r = 0; r < 4; r++) {
-                float v = red[((0 * C::kRedTiles + tt) * 4 + r) * 64 + lane];
+                float v = red[(((grp * WK + 0) * R + tt) * 4 + r) * 64 + lane];
 #pragma unroll
-                for (int w = 1; w < WAVES; w++)
-                    v += red[((w * C::kRedTiles + tt) * 4 + r) * 64 + lane];
+                for (int w = 1; w < WK; w++)
+                    v += red[(((grp * WK + w) * R + tt) * 4 + r) * 64 + lane];
                 const int rl = 4 * g + r;
                 if (rl < vrows[i])
-                    p.y[(row0 + i * 16 + rl) * p.ldy + col] = v * unscale;
+                    p.y[(row0 + (wm * TM + i) * 16 + rl) * p.ldy + col] = v * unscale;
             }
         }
         __syncthreads();
@@ -492,36 +536,45 @@ hipError_t launch_dense_cfg(const GemmProblem &p, hipStream_t stream)
     return launch_cfg<C, kGemm>(p, tm, tn, 0, 0, (int64_t)tm * tn, stream);
 }
 
-// Dense tile shapes (rows x columns), KC = 8 blocks per stage (2 per wave).
-// Two workgroups per CU.
+// Dense tile shapes.  Wide shapes run one 8-wave workgroup per CU whose
+// waves advance together through the stage barriers (two independent
+// workgroups on one CU finish at different times: the older one gets issue
+// priority and the younger then runs alone).  KC = 8 blocks per stage.
 template <int BITS> struct Tiles {
-    static constexpr int KC = 8;
-    // 8-bit codes double the A staging registers: the widest tile stages 4
-    // blocks at a time so that it still fits two workgroups per CU
-    using T64x80 = Cfg<BITS, 64, 80, BITS == 8 ? 4 : KC>;
-    using T64x64 = Cfg<BITS, 64, 64, KC>;
-    using T32x128 = Cfg<BITS, 32, 128, KC>;
-    using T16x64 = Cfg<BITS, 16, 64, KC>;
-    using T16x32 = Cfg<BITS, 16, 32, KC>;
-    using T64x32 = Cfg<BITS, 64, 32, KC>;
-    using T32x64 = Cfg<BITS, 32, 64, KC>;
+    // 64 x 160: two column halves of 64 x 80, K split in four (8-bit codes
+    // stage 4 blocks at a time to stay within 256 registers)
+    using W64x160 = Cfg<BITS, 4, 5, 1, 2, 4, BITS == 8 ? 4 : 8>;
+    // 64 x 128: two column halves of 64 x 64, K split in four
+    using W64x128 = Cfg<BITS, 4, 4, 1, 2, 4, 8>;
+    // 64 x 64: four waves, K split in four (two workgroups per CU)
+    using T64x64 = Cfg<BITS, 4, 4, 1, 1, 4, 8>;
+    using T64x32 = Cfg<BITS, 4, 2, 1, 1, 4, 8>;
+    // small M: 16 rows, K split in four
+    using T16x64 = Cfg<BITS, 1, 4, 1, 1, 4, 8>;
+    using T16x32 = Cfg<BITS, 1, 2, 1, 1, 4, 8>;
 };
 
 constexpr int kCUs = 256;
 
-// Pick the shape with the smallest estimated time: rounds of 2 workgroups per
-// CU times the per-tile cost, where the cost counts the epilogue (2 per sum)
-// plus operand unpacking (3 per row tile, 5 per column tile, per 16x16x32).
-inline double est(int64_t m, int64_t n, int bm, int bn)
+// Estimated time of a shape: rounds of resident workgroups times the
+// per-wave cost of one block (epilogue 8 per 16x16 tile, operand unpacking
+// 3 per row tile and 5 per column tile), divided by the waves per SIMD.
+inline double est(int64_t m, int64_t n, int bm, int bn, int tm, int tn, int per_cu,
+                  int waves_per_simd)
 {
     if (n % bn != 0)
         return 1e300;
     const int64_t tiles = ((m + bm - 1) / bm) * (n / bn);
-    const int64_t slots = 2 * kCUs;
+    const int64_t slots = (int64_t)per_cu * kCUs;
     const double rounds = (double)((tiles + slots - 1) / slots);
-    const double tm = bm / 16.0, tn = bn / 16.0;
-    const double cost = 8.0 * tm * tn + 3.0 * tm + 5.0 * tn;
-    return rounds * cost;
+    const double cost = 8.0 * tm * tn + 3.0 * tm + 5.0 * tn + 2.0 * tm * tn;
+    return rounds * cost * waves_per_simd;
+}
+
+template <class C>
+double est_cfg(int64_t m, int64_t n)
+{
+    return est(m, n, C::BM, C::BN, C::TM, C::TN, C::kOcc, C::kWaves * C::kOcc / 4);
 }
 
 template <int BITS>
@@ -530,26 +583,20 @@ hipError_t launch_dense_bits(const GemmProblem &p, hipStream_t stream)
     using T = Tiles<BITS>;
     const int64_t m = p.rows, n = p.n;
     if (m <= 16) {
-        if (est(m, n, 16, 64) <= est(m, n, 16, 32))
+        if (est_cfg<typename T::T16x64>(m, n) <= est_cfg<typename T::T16x32>(m, n))
             return launch_dense_cfg<typename T::T16x64>(p, stream);
         return launch_dense_cfg<typename T::T16x32>(p, stream);
     }
-    struct Cand { int bm, bn, id; };
-    const Cand cands[] = {{64, 80, 0}, {64, 64, 1}, {32, 128, 2}, {32, 64, 3}, {64, 32, 4}};
-    int best = 4;
-    double best_t = est(m, n, 64, 32);
-    for (const Cand &c : cands) {
-        const double t = est(m, n, c.bm, c.bn);
-        if (t < best_t) {
-            best_t = t;
-            best = c.id;
-        }
-    }
+    const double e[4] = {est_cfg<typename T::W64x160>(m, n), est_cfg<typename T::W64x128>(m, n),
+                         est_cfg<typename T::T64x64>(m, n), est_cfg<typename T::T64x32>(m, n)};
+    int best = 3;
+    for (int i = 0; i < 3; i++)
+        if (e[i] < e[best])
+            best = i;
     switch (best) {
-    case 0: return launch_dense_cfg<typename T::T64x80>(p, stream);
-    case 1: return launch_dense_cfg<typename T::T64x64>(p, stream);
-    case 2: return launch_dense_cfg<typename T::T32x128>(p, stream);
-    case 3: return launch_dense_cfg<typename T::T32x64>(p, stream);
+    case 0: return launch_dense_cfg<typename T::W64x160>(p, stream);
+    case 1: return launch_dense_cfg<typename T::W64x128>(p, stream);
+    case 2: return launch_dense_cfg<typename T::T64x64>(p, stream);
     default: return launch_dense_cfg<typename T::T64x32>(p, stream);
     }
 }
@@ -557,8 +604,8 @@ hipError_t launch_dense_bits(const GemmProblem &p, hipStream_t stream)
 template <int BITS>
 hipError_t launch_grouped_bits(const GemmProblem &p, hipStream_t stream)
 {
-    using C = Cfg<BITS, 32, 64, Tiles<BITS>::KC>;
-    using C32 = Cfg<BITS, 32, 32, Tiles<BITS>::KC>;
+    using C = Cfg<BITS, 2, 4, 1, 1, 4, 8>;  // 32 x 64
+    using C32 = Cfg<BITS, 2, 2, 1, 1, 4, 8>; // 32 x 32
     // every expert needs ceil(rows_e / BM) slots: bounded by both of these
     int64_t slots = (p.rows + p.experts * (C::BM - 1)) / C::BM;
     if (slots > p.rows)
@@ -574,7 +621,7 @@ hipError_t launch_grouped_bits(const GemmProblem &p, hipStream_t stream)
 template <int BITS>
 hipError_t launch_sums_bits(const GemmProblem &p, hipStream_t stream)
 {
-    using C = Cfg<BITS, 32, 32, Tiles<BITS>::KC>;
+    using C = Cfg<BITS, 2, 2, 1, 1, 4, 8>; // 32 x 32
     const int tm0 = (int)(p.m0 / C::BM), tm1 = (int)((p.m1 + C::BM - 1) / C::BM);
     const int tn0 = (int)(p.n0 / C::BN), tn1 = (int)((p.n1 + C::BN - 1) / C::BN);
     const int tm = tm1 - tm0, tn = tn1 - tn0;

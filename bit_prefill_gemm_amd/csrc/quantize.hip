@@ -73,24 +73,13 @@ __device__ __forceinline__ void load8(const uint16_t *src, int t, float (&v)[8])
     v[6] = bf16_to_f32(hi.y & 0xFFFFu); v[7] = bf16_to_f32(hi.y >> 16);
 }
 
-template <typename T, int BITS>
-__global__ __launch_bounds__(kThreads) void quantize_h32_kernel(
-    const T *__restrict__ x, int64_t k, int64_t ldx, int64_t nblk_total, int rotate,
-    uint8_t *__restrict__ codes, float *__restrict__ scales)
+// Rotate and quantize one block whose 8 values (this lane's share) are in v.
+template <int BITS>
+__device__ __forceinline__ void quantize_block(float (&v)[8], int t, int rotate, int64_t row,
+                                               int64_t b, int64_t k, int64_t nb,
+                                               uint8_t *__restrict__ codes,
+                                               float *__restrict__ scales)
 {
-    const int64_t blk = (int64_t)blockIdx.x * (kThreads / 4) + (threadIdx.x >> 2);
-    const int t = threadIdx.x & 3;
-    // All four lanes of a quad share `blk`, so a quad exits as a whole and the
-    // quad-local DPP exchanges below never read an exited lane.
-    if (blk >= nblk_total)
-        return;
-    const int64_t nb = k / 32;
-    const int64_t row = blk / nb;
-    const int64_t b = blk - row * nb;
-
-    float v[8];
-    load8(x + row * ldx + b * 32, t, v);
-
     if (rotate) {
         // h = 1: pairs (4t, 4t+1), (4t+2, 4t+3) and the same in the upper half
 #pragma unroll
@@ -163,6 +152,41 @@ __global__ __launch_bounds__(kThreads) void quantize_h32_kernel(
         scales[row * nb + b] = d;
 }
 
+// One quad of lanes per 32-block, grid-stride over the blocks of the matrix;
+// the next block's values are loaded before the current block's arithmetic.
+// All four lanes of a quad walk the same blocks and leave the loop together,
+// so the quad-local DPP exchanges never read an exited lane.
+template <typename T, int BITS>
+__global__ __launch_bounds__(kThreads) void quantize_h32_kernel(
+    const T *__restrict__ x, int64_t k, int64_t ldx, int64_t nblk_total, int rotate,
+    uint8_t *__restrict__ codes, float *__restrict__ scales)
+{
+    const int t = threadIdx.x & 3;
+    const int64_t stride = (int64_t)gridDim.x * (kThreads / 4);
+    const int64_t nb = k / 32;
+    int64_t blk = (int64_t)blockIdx.x * (kThreads / 4) + (threadIdx.x >> 2);
+    if (blk >= nblk_total)
+        return;
+    float v[8];
+    int64_t row = blk / nb;
+    load8(x + row * ldx + (blk - row * nb) * 32, t, v);
+    while (true) {
+        const int64_t cur_row = row, cur_b = blk - row * nb;
+        const int64_t next = blk + stride;
+        float nv[8];
+        if (next < nblk_total) {
+            row = next / nb;
+            load8(x + row * ldx + (next - row * nb) * 32, t, nv);
+        }
+        quantize_block<BITS>(v, t, rotate, cur_row, cur_b, k, nb, codes, scales);
+        if (next >= nblk_total)
+            break;
+        blk = next;
+        for (int i = 0; i < 8; i++)
+            v[i] = nv[i];
+    }
+}
+
 } // namespace
 
 hipError_t launch_quantize(const void *x, int dtype, int64_t m, int64_t k, int64_t ldx,
@@ -172,7 +196,9 @@ hipError_t launch_quantize(const void *x, int dtype, int64_t m, int64_t k, int64
     const int64_t nblk = m * (k / 32);
     if (nblk == 0)
         return hipSuccess;
-    const dim3 grid((unsigned)((nblk + kThreads / 4 - 1) / (kThreads / 4)));
+    // enough quads to fill every CU several times over; each walks blocks
+    const int64_t needed = (nblk + kThreads / 4 - 1) / (kThreads / 4);
+    const dim3 grid((unsigned)(needed < 2048 ? needed : 2048));
     uint8_t *c = static_cast<uint8_t *>(codes);
     if (dtype == 0 && act_bits == 4)
         quantize_h32_kernel<float, 4><<<grid, kThreads, 0, stream>>>(
