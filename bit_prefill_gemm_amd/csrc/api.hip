@@ -16,6 +16,7 @@
 namespace {
 
 constexpr int kMaxDevices = 64;
+constexpr int64_t kMaxGemmK = (int64_t)1 << 22;
 std::atomic<int> g_device_ok[kMaxDevices]; // 0 unknown, 1 gfx950, 2 other
 
 bpg_status check_device()
@@ -43,14 +44,17 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 bpg_status launch_status(hipError_t e) { return e == hipSuccess ? BPG_OK : BPG_ERR_LAUNCH; }
 
+// groups of four blocks per row
+int64_t block_groups(int64_t k) { return (k / 32 + 3) / 4; }
+
 uint64_t image_bytes(int64_t n, int64_t k, int64_t e)
 {
-    return (uint64_t)e * (uint64_t)n * (uint64_t)(k / 32) * 18u;
+    return (uint64_t)e * (uint64_t)(n / 32) * (uint64_t)block_groups(k) * 2304u;
 }
 
 uint64_t scales_offset(int64_t n, int64_t k, int64_t e)
 {
-    return (uint64_t)e * (uint64_t)n * (uint64_t)(k / 32) * 16u;
+    return (uint64_t)e * (uint64_t)(n / 32) * (uint64_t)block_groups(k) * 2048u;
 }
 
 bool shape_ok(int64_t n, int64_t k, int64_t e)
@@ -60,7 +64,7 @@ bool shape_ok(int64_t n, int64_t k, int64_t e)
     // keep every byte offset of the image inside int64 and every tile count in int
     if (n > (int64_t)1 << 30 || k > (int64_t)1 << 30 || e > (int64_t)1 << 20)
         return false;
-    const long double bytes = (long double)e * n * (k / 32) * 18;
+    const long double bytes = (long double)e * (n / 32) * block_groups(k) * 2304;
     return bytes < (long double)((uint64_t)1 << 62);
 }
 
@@ -70,7 +74,7 @@ bool shape_ok(int64_t n, int64_t k, int64_t e)
 bpg_status check_stamp(const bpg_weights_desc *w)
 {
     if (w->magic != BPG_WEIGHTS_MAGIC || w->version != BPG_WEIGHTS_VERSION ||
-        w->rotation != 32 || w->layout != BPG_LAYOUT_COLTILE32)
+        w->rotation != 32 || w->layout != BPG_LAYOUT_COLTILE32_K4)
         return BPG_ERR_STAMP;
     if (!shape_ok(w->n, w->k, w->num_experts))
         return BPG_ERR_STAMP;
@@ -92,7 +96,9 @@ bpg_status check_act(const void *codes, const float *scales, int act_bits, int64
         return BPG_ERR_NULL;
     if (!aligned16(codes) || !aligned16(scales))
         return BPG_ERR_ALIGN;
-    (void)k;
+    // the products address one workgroup's operands with 32-bit offsets
+    if (k > kMaxGemmK)
+        return BPG_ERR_SHAPE;
     return BPG_OK;
 }
 
@@ -155,13 +161,17 @@ void quantize_weight_block(const double in[32], uint8_t blk[18])
         blk[2 + j] = (uint8_t)(u[j] | (u[j + 16] << 4));
 }
 
-// Place one canonical 18-byte block of (expert e, row n, block b) in the image.
+// Place one canonical 18-byte block of (expert e, row n, block b) in the
+// image: its four code dwords go to slots s = 0..3 of (tile, group), the
+// scale next to the scales of the group's other blocks.
 inline void place_block(const uint8_t blk[18], int64_t e, int64_t n, int64_t b, int64_t N,
-                        int64_t B, uint8_t *codes, uint16_t *scales)
+                        int64_t G, uint8_t *codes, uint16_t *scales)
 {
-    const int64_t t = (e * (N / 32) + n / 32) * B + b; // (expert, column tile, block)
-    std::memcpy(codes + (t * 32 + n % 32) * 16, blk + 2, 16);
-    scales[t * 32 + n % 32] = (uint16_t)(blk[0] | (blk[1] << 8));
+    const int64_t tg = (e * (N / 32) + n / 32) * G + b / 4; // (expert, column tile, group)
+    const int64_t c = n % 32, q = b % 4;
+    for (int s = 0; s < 4; s++)
+        std::memcpy(codes + tg * 2048 + ((s * 32 + c) * 4 + q) * 4, blk + 2 + 4 * s, 4);
+    scales[tg * 128 + c * 4 + q] = (uint16_t)(blk[0] | (blk[1] << 8));
 }
 
 } // namespace
@@ -205,9 +215,13 @@ bpg_status rotate_pack_weights(const void *src, bpg_src_kind kind, int64_t n, in
     if (dst_bytes < total)
         return BPG_ERR_BUFFER;
 
-    const int64_t B = k / 32;
+    const int64_t B = k / 32, G = block_groups(k);
     uint8_t *codes = static_cast<uint8_t *>(dst_host);
-    uint16_t *scales = reinterpret_cast<uint16_t *>(codes + scales_offset(n, k, num_experts));
+    const uint64_t soff = scales_offset(n, k, num_experts);
+    uint16_t *scales = reinterpret_cast<uint16_t *>(codes + soff);
+    // blocks past B: codes 0x88 (value 0), scale 0
+    std::memset(codes, 0x88, soff);
+    std::memset(codes + soff, 0, total - soff);
     for (int64_t e = 0; e < num_experts; e++)
         for (int64_t r = 0; r < n; r++)
             for (int64_t b = 0; b < B; b++) {
@@ -230,7 +244,7 @@ bpg_status rotate_pack_weights(const void *src, bpg_src_kind kind, int64_t n, in
                     }
                     quantize_weight_block(in, blk);
                 }
-                place_block(blk, e, r, b, n, B, codes, scales);
+                place_block(blk, e, r, b, n, G, codes, scales);
             }
 
     bpg_weights_desc d;
@@ -238,7 +252,7 @@ bpg_status rotate_pack_weights(const void *src, bpg_src_kind kind, int64_t n, in
     d.magic = BPG_WEIGHTS_MAGIC;
     d.version = BPG_WEIGHTS_VERSION;
     d.rotation = 32;
-    d.layout = BPG_LAYOUT_COLTILE32;
+    d.layout = BPG_LAYOUT_COLTILE32_K4;
     d.n = n;
     d.k = k;
     d.num_experts = num_experts;
@@ -359,7 +373,7 @@ bpg_status w4a4_gemm_blocksums(const void *codes, const float *scales, int act_b
     if (act_bits != 4 && act_bits != 8)
         return BPG_ERR_DTYPE;
     if (m < 0 || expert < 0 || expert >= w->num_experts || m0 < 0 || m0 > m1 || m1 > m ||
-        n0 < 0 || n0 > n1 || n1 > w->n || m > ((int64_t)1 << 31) - 1)
+        n0 < 0 || n0 > n1 || n1 > w->n || m > ((int64_t)1 << 31) - 1 || w->k > kMaxGemmK)
         return BPG_ERR_SHAPE;
     if (!codes || !w_dev || !sums)
         return BPG_ERR_NULL;

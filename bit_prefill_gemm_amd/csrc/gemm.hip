@@ -5,8 +5,10 @@
 // Q4_0 code u means u-8, which is the code with its top bit flipped read as a
 // 4-bit two's-complement number, so the kernel reads Q4_0 nibbles bit for bit.
 // gfx950 has no int4 matrix instruction: both operands are widened to int8 in
-// registers and every 32-value block is one v_mfma_i32_16x16x32_i8 per 16x16
-// output tile (K = 32 is exactly one block, so each result is one block sum).
+// registers, and every 32-value block is one integer matrix instruction per
+// output tile with K = 32 (so each result is exactly one block sum):
+// v_mfma_i32_32x32x32_i8 (32x32 tiles, the double-rate gfx950 form) for the
+// wide shapes, v_mfma_i32_16x16x32_i8 (16x16 tiles) for short or ragged ones.
 //
 // Per K-block b the kernel needs y[m][n] += da[m][b] * dw[n][b] * S[m][n][b]
 // with S the exact int32 block dot product:
@@ -18,15 +20,15 @@
 //   - t = fma(F, dw, -12582912*dw) = 256*S*dw (the constant product is exact:
 //     dw is an fp16 value, 11 significant bits), then acc = fma(t, da, acc).
 // Two fp32 VALU operations per (m, n, b) and no integer conversion.  Packed
-// fp32 is not used, so that epilogue, not the matrix core, bounds the kernel:
-// one 16x16x32 instruction yields 256 sums = 8 VALU instructions per wave.
+// fp32 is not used, so that epilogue, not the matrix core, bounds the kernel.
 //
-// Work split: a workgroup owns a BM x BN output tile; its 4 waves each take
-// every 4th K-block of a stage and keep partial sums of the whole tile, which
-// are added in a fixed order (wave 0, 1, 2, 3) through LDS at the end, so the
-// result is bit-identical from run to run.  Operands are staged through LDS,
-// KC blocks per stage, double buffered, with the next stage's global loads in
-// flight during the current stage's arithmetic.  Two workgroups fit on a CU.
+// Work split: a workgroup owns a BM x BN output tile split among WM x WN wave
+// groups; the WK waves of a group each take every WK-th block of a stage and
+// keep partial sums of the group's tile, which are added in a fixed order
+// (wave 0, 1, ...) through LDS at the end, so the result is bit-identical from
+// run to run.  Operands are staged through LDS, KC blocks per stage, double
+// buffered, with the next stage's global loads in flight during the current
+// stage's arithmetic.
 //
 // The same main loop also runs in block-sum mode (exact int32 S for parity
 // checks) and in grouped mode (rows sorted by expert, ragged row ranges).
@@ -42,22 +44,24 @@ namespace bpg {
 namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
 
 constexpr int kMagicBits = 0x4B400000;
 constexpr float kMagic = 12582912.0f;
 
 enum Mode { kGemm = 0, kGrouped = 1, kSums = 2 };
 
-// Wave layout: WM x WN x WK waves; wave (wm, wn, wk) owns the TM x TN
-// 16x16 tiles at row tile wm*TM and column tile wn*TN of the workgroup tile
-// and every WK-th block of a stage (the K split).
-template <int BITS_, int TM_, int TN_, int WM_, int WN_, int WK_, int KC_>
+// MF: matrix instruction tile (16 or 32).  Wave layout: WM x WN x WK waves;
+// wave (wm, wn, wk) owns the TM x TN tiles of MF x MF at row tile wm*TM and
+// column tile wn*TN of the workgroup tile, and every WK-th block of a stage.
+template <int BITS_, int MF_, int TM_, int TN_, int WM_, int WN_, int WK_, int KC_>
 struct Cfg {
-    static constexpr int BITS = BITS_, TM = TM_, TN = TN_, KC = KC_;
+    static constexpr int BITS = BITS_, MF = MF_, TM = TM_, TN = TN_, KC = KC_;
     static constexpr int WM = WM_, WN = WN_, WK = WK_;
     static constexpr int kWaves = WM * WN * WK;
     static constexpr int kThreads = 64 * kWaves;
-    static constexpr int BM = 16 * TM * WM, BN = 16 * TN * WN;
+    static constexpr int BM = MF * TM * WM, BN = MF * TN * WN;
+    static constexpr int kRegs = MF * MF / 64;        // output registers per tile and lane
     static constexpr int kAB = BITS == 4 ? 16 : 32;   // code bytes per (row, block)
     static constexpr int kShift = BITS == 4 ? 8 : 4;  // log2 of the operand widening
     // one stage in LDS: A codes [KC][BM][kAB], W codes [KC][BN][16],
@@ -69,9 +73,10 @@ struct Cfg {
     static constexpr int kStage = kLdsA + kLdsW + kLdsDa + kLdsDw;
     static constexpr int kTiles = TM * TN; // per wave
     // final reduction: every wave parks the partial sums of up to kRedTiles
-    // of its tiles at a time ([group][wk][tile][4 regs][64 lanes] fp32)
-    static constexpr int kRedTiles = kTiles < 16 ? kTiles : 16;
-    static constexpr int kLdsRed = kWaves * kRedTiles * 4 * 64 * 4;
+    // of its tiles at a time ([group][wk][tile][kRegs][64 lanes] fp32)
+    static constexpr int kRedCap = MF == 16 ? 16 : 4;
+    static constexpr int kRedTiles = kTiles < kRedCap ? kTiles : kRedCap;
+    static constexpr int kLdsRed = kWaves * kRedTiles * kRegs * 64 * 4;
     static constexpr int kLds = 2 * kStage > kLdsRed ? 2 * kStage : kLdsRed;
     // 16-byte global chunks per stage and per thread
     static constexpr int kChA = BM * KC * (kAB / 16);
@@ -79,27 +84,26 @@ struct Cfg {
     static constexpr int kPtA = (kChA + kThreads - 1) / kThreads;
     static constexpr int kPtW = (kChW + kThreads - 1) / kThreads;
     static constexpr int kPtDa = (BM * KC + kThreads - 1) / kThreads;
-    static constexpr int kPtDw = (BN * KC + kThreads - 1) / kThreads;
+    static constexpr int kChDw = BN * KC / 4; // 8-byte chunks: four blocks' scales
+    static constexpr int kPtDw = (kChDw + kThreads - 1) / kThreads;
     static constexpr int kOcc = kThreads >= 512 ? 1 : 2; // workgroups per CU aimed at
-    static_assert(KC % WK == 0, "K split");
+    static_assert(MF == 16 || MF == 32, "matrix tile");
+    static_assert(KC % WK == 0 && KC <= 8, "K split and swizzle range");
+    static_assert(KC % 4 == 0, "stages hold whole groups of four blocks");
     static_assert(kLds <= 160 * 1024, "LDS budget");
 };
 
 // Activation nibbles (two's complement) of one dword -> 8 int8 = 16 * value:
-// low nibbles (elements 4g..4g+3) then high nibbles (elements 16+4g..16+4g+3).
-__device__ __forceinline__ long widen_act4(uint32_t d)
-{
-    const uint32_t lo = (d << 4) & 0xF0F0F0F0u;
-    const uint32_t hi = d & 0xF0F0F0F0u;
-    return (long)(((uint64_t)hi << 32) | lo);
-}
+// low nibbles first, then high nibbles.
+__device__ __forceinline__ uint32_t act_lo(uint32_t d) { return (d << 4) & 0xF0F0F0F0u; }
+__device__ __forceinline__ uint32_t act_hi(uint32_t d) { return d & 0xF0F0F0F0u; }
+// Q4_0 nibbles u -> top bit flipped (u XOR 8 is u-8 in two's complement) ->
+// 16*(u-8).
+__device__ __forceinline__ uint32_t q40_lo(uint32_t d) { return ((d << 4) ^ 0x80808080u) & 0xF0F0F0F0u; }
+__device__ __forceinline__ uint32_t q40_hi(uint32_t d) { return (d ^ 0x88888888u) & 0xF0F0F0F0u; }
 
-// Q4_0 nibbles u -> top bit flipped (u XOR 8 is u-8 in two's complement) -> 16*(u-8).
-// Each half is one shift at most plus one three-input bit operation.
-__device__ __forceinline__ long widen_q4_0(uint32_t d)
+__device__ __forceinline__ long pack2(uint32_t lo, uint32_t hi)
 {
-    const uint32_t lo = ((d << 4) ^ 0x80808080u) & 0xF0F0F0F0u;
-    const uint32_t hi = (d ^ 0x88888888u) & 0xF0F0F0F0u;
     return (long)(((uint64_t)hi << 32) | lo);
 }
 
@@ -107,6 +111,14 @@ __device__ __forceinline__ float half_bits_to_float(uint16_t h)
 {
     return (float)__builtin_bit_cast(_Float16, h);
 }
+
+// LDS slot of activation row `r` of block `kc`: the low four bits are
+// XOR-swizzled so that both the staging writes (8 consecutive lanes write the
+// 8 blocks of one row, 16 lanes two rows) and the operand reads (consecutive
+// rows of one block) spread over the banks.  A bijection inside every aligned
+// group of 16.  Weight columns need none: their staging writes one dword
+// slot of 16 consecutive columns at a time.
+__device__ __forceinline__ int swz(int r, int kc) { return r ^ kc ^ ((r & 1) << 3); }
 
 // Workgroups are dispatched round-robin over the 8 XCDs (w % 8 selects the
 // XCD).  Hand each XCD a contiguous range of logical tiles, so tiles that
@@ -171,25 +183,64 @@ __device__ bool grouped_slot(const int32_t *__restrict__ off, int64_t experts, i
     return true;
 }
 
+// Operand and result registers of the two matrix instruction shapes.
+template <int MF> struct Mfma;
+
+template <> struct Mfma<16> {
+    typedef long Op;
+    typedef v4i Acc;
+    // lane l: row / column l % 16 of the tile and K group g = l / 16, which
+    // holds bytes 4g..4g+3 of the packed block (elements 4g..4g+3 from the
+    // low nibbles, 16+4g..16+4g+3 from the high ones); result register r of
+    // lane l is row 4g + r, column l % 16.
+    static __device__ __forceinline__ int rc(int lane) { return lane & 15; }
+    static __device__ __forceinline__ int kg(int lane) { return lane >> 4; }
+    static __device__ __forceinline__ int out_row(int g, int r) { return 4 * g + r; }
+    static __device__ __forceinline__ Acc mma(Op a, Op b, Acc c)
+    {
+        return __builtin_amdgcn_mfma_i32_16x16x32_i8(a, b, c, 0, 0, 0);
+    }
+};
+
+template <> struct Mfma<32> {
+    typedef v4i Op;
+    typedef v16i Acc;
+    // lane l: row / column l % 32 of the tile and K half g = l / 32, which
+    // holds bytes 8g..8g+7 of the packed block (elements 8g..8g+7 low,
+    // 16+8g..16+8g+7 high); result register r of lane l is row
+    // 8 (r / 4) + 4g + r % 4, column l % 32.
+    static __device__ __forceinline__ int rc(int lane) { return lane & 31; }
+    static __device__ __forceinline__ int kg(int lane) { return lane >> 5; }
+    static __device__ __forceinline__ int out_row(int g, int r) { return 8 * (r >> 2) + 4 * g + (r & 3); }
+    static __device__ __forceinline__ Acc mma(Op a, Op b, Acc c)
+    {
+        return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
+    }
+};
+
 template <class C, int MODE>
 __global__ __launch_bounds__(C::kThreads, C::kOcc) void w4a4_kernel(GemmProblem p, int tiles_m,
                                                               int tiles_n, int tm0, int tn0)
 {
-    constexpr int BM = C::BM, BN = C::BN, KC = C::KC, TM = C::TM, TN = C::TN;
-    constexpr int NT = C::kThreads, kAB = C::kAB, WK = C::WK;
+    constexpr int BM = C::BM, BN = C::BN, KC = C::KC, TM = C::TM, TN = C::TN, MF = C::MF;
+    constexpr int NT = C::kThreads, kAB = C::kAB, WK = C::WK, RG = C::kRegs;
+    typedef Mfma<MF> M;
+    typedef typename M::Op Op;
+    typedef typename M::Acc Acc;
     __shared__ __attribute__((aligned(16))) uint8_t lds[C::kLds];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int j16 = lane & 15; // row (A operand) / column (B operand, output) in a 16-tile
-    const int g = lane >> 4;   // K group of the operands; output rows 4g..4g+3
+    const int rc = M::rc(lane); // operand row / column, result column, inside a tile
+    const int g = M::kg(lane);  // operand K group, result row group
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wk = wave % C::WK;
     const int wn = (wave / C::WK) % C::WN;
     const int wm = wave / (C::WK * C::WN);
     const int grp = wm * C::WN + wn; // waves of one group share tiles, split K
 
-    const int64_t B = p.k / 32;
+    const int B = (int)(p.k / 32); // the host limits K to 2^22
+    const int NG = (B + 3) / 4;     // groups of four blocks in the weight image
     const int64_t ntiles32 = p.n / 32;
 
     // ---- the tile of this workgroup
@@ -212,19 +263,19 @@ __global__ __launch_bounds__(C::kThreads, C::kOcc) void w4a4_kernel(GemmProblem 
 
     // ---- staging addresses, computed once.  Global reads are coalesced
     //      (consecutive threads read consecutive blocks of a row, or
-    //      consecutive columns); LDS slots are XOR-swizzled so that both these
-    //      writes and the MFMA operand reads spread over all banks.  Rows past
+    //      consecutive columns); LDS slots are swizzled (swz).  Rows past
     //      row_end are clamped to the last valid row: their values only reach
     //      output rows that are never stored.
+    // (every offset below stays under 2^31 for K <= 2^22)
     const uint8_t *__restrict__ a_base0 = p.codes + row0 * arow_bytes;
-    const uint8_t *__restrict__ w_base0 = p.wcodes + (expert * ntiles32 + ct0) * B * 512;
+    const uint8_t *__restrict__ w_base0 = p.wcodes + (expert * ntiles32 + ct0) * NG * 2048;
     const float *__restrict__ da_base0 = p.scales + row0 * B;
-    const uint16_t *__restrict__ dw_base0 = p.wscales + (expert * ntiles32 + ct0) * B * 32;
+    const uint16_t *__restrict__ dw_base0 = p.wscales + (expert * ntiles32 + ct0) * NG * 128;
     const int last_row = (int)(row_end - 1 - row0); // >= 0
 
     uint32_t oa[C::kPtA], la[C::kPtA], ow[C::kPtW], lw[C::kPtW];
     uint32_t oda[C::kPtDa], lda_[C::kPtDa], odw[C::kPtDw], ldw_[C::kPtDw];
-    int8_t kca[C::kPtA], kcw[C::kPtW], kcda[C::kPtDa], kcdw[C::kPtDw]; // block of each chunk
+    int8_t kca[C::kPtA], kcw[C::kPtW], kcda[C::kPtDa], kcdw[C::kPtDw]; // first block of each chunk
 #pragma unroll
     for (int i = 0; i < C::kPtA; i++) {
         const int c = tid + i * NT;
@@ -234,7 +285,9 @@ __global__ __launch_bounds__(C::kThreads, C::kOcc) void w4a4_kernel(GemmProblem 
         const int kc = rem / (kAB / 16), part = rem % (kAB / 16);
         const int rrow = row < last_row ? row : last_row;
         oa[i] = (uint32_t)(rrow * arow_bytes + kc * kAB + part * 16);
-        const int srow = kAB == 16 ? (row ^ kc ^ ((row & 1) << 3)) : (row ^ kc);
+        const int srow = swz(row, kc);
+        // 8-bit codes: the two 16-byte halves of a row block swap places on
+        // every other group of 8 rows (reads of 16 rows then avoid conflicts)
         const int slot = kAB == 32 ? (part ^ ((srow >> 3) & 1)) : 0;
         la[i] = (uint32_t)((kc * BM + srow) * kAB + slot * 16);
         kca[i] = (int8_t)(c < C::kChA ? kc : 127);
@@ -242,12 +295,13 @@ __global__ __launch_bounds__(C::kThreads, C::kOcc) void w4a4_kernel(GemmProblem 
 #pragma unroll
     for (int i = 0; i < C::kPtW; i++) {
         const int c = tid + i * NT;
+        // chunk: slot s of column col for the four blocks of group gs
         const int cc = c < C::kChW ? c : 0;
-        const int col = cc / KC, kc = cc % KC;
+        const int s = cc & 3, col = (cc >> 2) % BN, gs = (cc >> 2) / BN;
         const int64_t gcol = col0 + col;
-        ow[i] = (uint32_t)((((gcol >> 5) - ct0) * B + kc) * 512 + (gcol & 31) * 16);
-        lw[i] = (uint32_t)((kc * BN + (col ^ kc ^ ((col & 1) << 3))) * 16);
-        kcw[i] = (int8_t)(c < C::kChW ? kc : 127);
+        ow[i] = (uint32_t)((((gcol >> 5) - ct0) * NG + gs) * 2048 + (s * 32 + (gcol & 31)) * 16);
+        lw[i] = (uint32_t)((4 * gs * BN + col) * 16 + 4 * s); // block 4*gs; + q*BN*16 for 4*gs+q
+        kcw[i] = (int8_t)(c < C::kChW ? 4 * gs : 127);
     }
 #pragma unroll
     for (int i = 0; i < C::kPtDa; i++) {
@@ -262,46 +316,50 @@ __global__ __launch_bounds__(C::kThreads, C::kOcc) void w4a4_kernel(GemmProblem 
 #pragma unroll
     for (int i = 0; i < C::kPtDw; i++) {
         const int c = tid + i * NT;
-        const int cc = c < BN * KC ? c : 0;
-        const int kc = cc / BN, col = cc % BN;
+        // chunk: the scales of column col for the four blocks of group gs
+        const int cc = c < C::kChDw ? c : 0;
+        const int gs = cc / BN, col = cc % BN;
         const int64_t gcol = col0 + col;
-        odw[i] = (uint32_t)((((gcol >> 5) - ct0) * B + kc) * 32 + (gcol & 31));
-        ldw_[i] = (uint32_t)(kc * BN + col);
-        kcdw[i] = (int8_t)(c < BN * KC ? kc : 127);
+        odw[i] = (uint32_t)((((gcol >> 5) - ct0) * NG + gs) * 128 + (gcol & 31) * 4);
+        ldw_[i] = (uint32_t)(4 * gs * BN + col);
+        kcdw[i] = (int8_t)(c < C::kChDw ? 4 * gs : 127);
     }
 
     // ---- global -> registers -> LDS staging of one stage (KC blocks)
     uint4 ra[C::kPtA], rw[C::kPtW];
     float rda[C::kPtDa];
-    uint16_t rdw[C::kPtDw];
+    uint2 rdw[C::kPtDw];
 
     // Chunk i of a thread exists for every thread when (i+1)*NT <= count;
     // only the last chunk of a region can exist for some threads only.
 #define BPG_CHUNK_OK(i, count) ((((i) + 1) * NT <= (count)) || (tid + (i) * NT < (count)))
     // Full stages read every chunk; the last, partial stage skips blocks past K.
-    auto load_stage = [&](int64_t kb0, auto full_tag) {
+    // A thread whose last chunk does not exist reads chunk 0 instead (its
+    // offsets were set so) and never stores it: loads without a lane mask keep
+    // the waits before the stores simple.
+    auto load_stage = [&](int kb0, auto full_tag) {
         constexpr bool full = decltype(full_tag)::value;
-        const int kv = full ? KC : (int)(B - kb0);
+        const int kv = full ? KC : B - kb0;
         const uint8_t *ab = a_base0 + kb0 * kAB;
         const uint8_t *wb = w_base0 + kb0 * 512;
         const float *dab = da_base0 + kb0;
-        const uint16_t *dwb = dw_base0 + kb0 * 32;
+        const uint16_t *dwb = dw_base0 + kb0 * 32; // kb0 / 4 groups of 128 scales
 #pragma unroll
         for (int i = 0; i < C::kPtA; i++)
-            ra[i] = (BPG_CHUNK_OK(i, C::kChA) && (full || kca[i] < kv))
+            ra[i] = (full || kca[i] < kv)
                         ? *reinterpret_cast<const uint4 *>(ab + oa[i]) : make_uint4(0, 0, 0, 0);
 #pragma unroll
         for (int i = 0; i < C::kPtW; i++)
-            rw[i] = (BPG_CHUNK_OK(i, C::kChW) && (full || kcw[i] < kv))
+            rw[i] = (full || kcw[i] < kv)
                         ? *reinterpret_cast<const uint4 *>(wb + ow[i]) : make_uint4(0, 0, 0, 0);
         if (MODE != kSums) { // block sums never read scales
 #pragma unroll
             for (int i = 0; i < C::kPtDa; i++)
-                rda[i] = (BPG_CHUNK_OK(i, BM * KC) && (full || kcda[i] < kv)) ? dab[oda[i]] : 0.0f;
+                rda[i] = (full || kcda[i] < kv) ? dab[oda[i]] : 0.0f;
 #pragma unroll
             for (int i = 0; i < C::kPtDw; i++)
-                rdw[i] = (BPG_CHUNK_OK(i, BN * KC) && (full || kcdw[i] < kv)) ? dwb[odw[i]]
-                                                                               : (uint16_t)0;
+                rdw[i] = (full || kcdw[i] < kv)
+                             ? *reinterpret_cast<const uint2 *>(dwb + odw[i]) : make_uint2(0, 0);
         }
     };
 
@@ -315,8 +373,12 @@ __global__ __launch_bounds__(C::kThreads, C::kOcc) void w4a4_kernel(GemmProblem 
                 *reinterpret_cast<uint4 *>(A + la[i]) = ra[i];
 #pragma unroll
         for (int i = 0; i < C::kPtW; i++)
-            if (BPG_CHUNK_OK(i, C::kChW))
-                *reinterpret_cast<uint4 *>(W + lw[i]) = rw[i];
+            if (BPG_CHUNK_OK(i, C::kChW)) {
+                const uint32_t v[4] = {rw[i].x, rw[i].y, rw[i].z, rw[i].w};
+#pragma unroll
+                for (int q = 0; q < 4; q++)
+                    *reinterpret_cast<uint32_t *>(W + lw[i] + q * BN * 16) = v[q];
+            }
         if (MODE != kSums) {
 #pragma unroll
             for (int i = 0; i < C::kPtDa; i++)
@@ -324,85 +386,118 @@ __global__ __launch_bounds__(C::kThreads, C::kOcc) void w4a4_kernel(GemmProblem 
                     Da[lda_[i]] = rda[i];
 #pragma unroll
             for (int i = 0; i < C::kPtDw; i++)
-                if (BPG_CHUNK_OK(i, BN * KC)) {
-                    const float dw = half_bits_to_float(rdw[i]);
-                    Dw[ldw_[i]] = make_float2(dw, -kMagic * dw);
+                if (BPG_CHUNK_OK(i, C::kChDw)) {
+                    const uint16_t h[4] = {(uint16_t)(rdw[i].x & 0xFFFFu), (uint16_t)(rdw[i].x >> 16),
+                                           (uint16_t)(rdw[i].y & 0xFFFFu), (uint16_t)(rdw[i].y >> 16)};
+#pragma unroll
+                    for (int q = 0; q < 4; q++) {
+                        const float dw = half_bits_to_float(h[q]);
+                        Dw[ldw_[i] + q * BN] = make_float2(dw, -kMagic * dw);
+                    }
                 }
         }
     };
 #undef BPG_CHUNK_OK
 
-    // 16-row tiles of the workgroup tile that hold data (uniform per workgroup)
+    // rows of each of this wave's row tiles that hold data (uniform per wave)
     int vrows[TM];
 #pragma unroll
     for (int i = 0; i < TM; i++) {
-        const int64_t v = row_end - (row0 + (int64_t)(wm * TM + i) * 16);
-        vrows[i] = v < 0 ? 0 : (v > 16 ? 16 : (int)v);
+        const int64_t v = row_end - (row0 + (int64_t)(wm * TM + i) * MF);
+        vrows[i] = v < 0 ? 0 : (v > MF ? MF : (int)v);
     }
 
-    float acc[TM][TN][4];
+    float acc[TM][TN][RG];
 #pragma unroll
     for (int i = 0; i < TM; i++)
 #pragma unroll
         for (int j = 0; j < TN; j++)
 #pragma unroll
-            for (int r = 0; r < 4; r++)
+            for (int r = 0; r < RG; r++)
                 acc[i][j][r] = 0.0f;
 
-    v4i magic;
+    Acc magic;
 #pragma unroll
-    for (int r = 0; r < 4; r++)
+    for (int r = 0; r < RG; r++)
         magic[r] = kMagicBits;
 
-    const int64_t nstages = (B + KC - 1) / KC;
-    if (KC <= B)
-        load_stage(0, std::true_type{});
-    else
-        load_stage(0, std::false_type{});
-    store_stage(lds);
-    __syncthreads();
+    // matrix operands of row `srow` / column `scol` (LDS slots) of block kc
+    auto load_a = [&](const uint8_t *A, int kc, int srow) -> Op {
+        const uint8_t *rowp = A + (kc * BM + srow) * kAB;
+        if constexpr (MF == 16) {
+            if constexpr (kAB == 16) {
+                const uint32_t d = *reinterpret_cast<const uint32_t *>(rowp + 4 * g);
+                return pack2(act_lo(d), act_hi(d));
+            } else {
+                const int sw = (srow >> 3) & 1;
+                const uint32_t lo = *reinterpret_cast<const uint32_t *>(rowp + sw * 16 + 4 * g);
+                const uint32_t hi = *reinterpret_cast<const uint32_t *>(rowp + (sw ^ 1) * 16 + 4 * g);
+                return pack2(lo, hi);
+            }
+        } else {
+            Op o;
+            if constexpr (kAB == 16) {
+                const uint2 d = *reinterpret_cast<const uint2 *>(rowp + 8 * g);
+                o[0] = (int)act_lo(d.x);
+                o[1] = (int)act_lo(d.y);
+                o[2] = (int)act_hi(d.x);
+                o[3] = (int)act_hi(d.y);
+            } else {
+                const int sw = (srow >> 3) & 1;
+                const uint2 lo = *reinterpret_cast<const uint2 *>(rowp + sw * 16 + 8 * g);
+                const uint2 hi = *reinterpret_cast<const uint2 *>(rowp + (sw ^ 1) * 16 + 8 * g);
+                o[0] = (int)lo.x;
+                o[1] = (int)lo.y;
+                o[2] = (int)hi.x;
+                o[3] = (int)hi.y;
+            }
+            return o;
+        }
+    };
+    auto load_b = [&](const uint8_t *W, int kc, int scol) -> Op {
+        const uint8_t *colp = W + (kc * BN + scol) * 16;
+        if constexpr (MF == 16) {
+            const uint32_t d = *reinterpret_cast<const uint32_t *>(colp + 4 * g);
+            return pack2(q40_lo(d), q40_hi(d));
+        } else {
+            const uint2 d = *reinterpret_cast<const uint2 *>(colp + 8 * g);
+            Op o;
+            o[0] = (int)q40_lo(d.x);
+            o[1] = (int)q40_lo(d.y);
+            o[2] = (int)q40_hi(d.x);
+            o[3] = (int)q40_hi(d.y);
+            return o;
+        }
+    };
 
     // One stage of arithmetic on the operands held in buffer A.
-    auto compute_stage = [&](const uint8_t *A, int64_t kb0) {
+    auto compute_stage = [&](const uint8_t *A, int kb0) {
         const uint8_t *W = A + C::kLdsA;
         const float *Da = reinterpret_cast<const float *>(W + C::kLdsW);
         const float2 *Dw = reinterpret_cast<const float2 *>(W + C::kLdsW + C::kLdsDa);
-        const int64_t kvalid = B - kb0; // >= 1
+        const int kvalid = B - kb0; // >= 1
 
 #pragma unroll
         for (int kk = 0; kk < KC / WK; kk++) {
             const int kc = kk * WK + wk;
             if (kc >= kvalid)
                 break;
-            // A operands: row j16 of each 16-row tile, K group g
-            // swizzled slot of row/column j16 of every 16-tile for this block
-            const int sw16 = kAB == 16 ? (j16 ^ kc ^ ((j16 & 1) << 3)) : (j16 ^ kc);
-            const int swc = j16 ^ kc ^ ((j16 & 1) << 3);
-            long a[TM];
+            Op a[TM];
 #pragma unroll
-            for (int i = 0; i < TM; i++) {
-                if (kAB == 16) {
-                    a[i] = widen_act4(*reinterpret_cast<const uint32_t *>(A + (kc * BM + (wm * TM + i) * 16 + sw16) * 16 + 4 * g));
-                } else {
-                    const int srow = (wm * TM + i) * 16 + sw16;
-                    const int sw = (srow >> 3) & 1;
-                    const uint32_t lo = *reinterpret_cast<const uint32_t *>(A + (kc * BM + srow) * 32 + (sw * 16) + 4 * g);
-                    const uint32_t hi = *reinterpret_cast<const uint32_t *>(A + (kc * BM + srow) * 32 + ((sw ^ 1) * 16) + 4 * g);
-                    a[i] = (long)(((uint64_t)hi << 32) | lo);
-                }
-            }
+            for (int i = 0; i < TM; i++)
+                a[i] = load_a(A, kc, swz((wm * TM + i) * MF + rc, kc));
 
             if (MODE == kSums) {
 #pragma unroll
                 for (int j = 0; j < TN; j++) {
-                    const long b = widen_q4_0(*reinterpret_cast<const uint32_t *>(W + (kc * BN + (wn * TN + j) * 16 + swc) * 16 + 4 * g));
-                    const int64_t col = col0 + (wn * TN + j) * 16 + j16;
+                    const Op b = load_b(W, kc, (wn * TN + j) * MF + rc);
+                    const int64_t col = col0 + (wn * TN + j) * MF + rc;
 #pragma unroll
                     for (int i = 0; i < TM; i++) {
-                        const v4i D = __builtin_amdgcn_mfma_i32_16x16x32_i8(a[i], b, magic, 0, 0, 0);
+                        const Acc D = M::mma(a[i], b, magic);
 #pragma unroll
-                        for (int r = 0; r < 4; r++) {
-                            const int64_t row = row0 + (wm * TM + i) * 16 + 4 * g + r;
+                        for (int r = 0; r < RG; r++) {
+                            const int64_t row = row0 + (wm * TM + i) * MF + M::out_row(g, r);
                             if (row >= p.m0 && row < p.m1 && col >= p.n0 && col < p.n1)
                                 p.sums[((row - p.m0) * (p.n1 - p.n0) + (col - p.n0)) * B + kb0 + kc] =
                                     (D[r] - kMagicBits) >> C::kShift;
@@ -410,35 +505,43 @@ __global__ __launch_bounds__(C::kThreads, C::kOcc) void w4a4_kernel(GemmProblem 
                     }
                 }
             } else {
-                float4 da[TM];
+                // row scales of the lane's result rows, four consecutive rows at a time
+                float4 da[TM][RG / 4];
 #pragma unroll
                 for (int i = 0; i < TM; i++)
-                    da[i] = *reinterpret_cast<const float4 *>(Da + kc * BM + (wm * TM + i) * 16 + 4 * g);
+#pragma unroll
+                    for (int q = 0; q < RG / 4; q++)
+                        da[i][q] = *reinterpret_cast<const float4 *>(
+                            Da + kc * BM + (wm * TM + i) * MF + M::out_row(g, 4 * q));
                 // Software pipeline over the column tiles: the matrix
                 // instructions of tile j are issued before the epilogue of
                 // tile j-1, so their latency hides behind VALU work.  Padded
                 // rows (past row_end) are computed too and never stored.
-                v4i Dp[TM];
+                Acc Dp[TM];
                 float2 dwp = make_float2(0.0f, 0.0f);
 #pragma unroll
                 for (int j = 0; j <= TN; j++) {
-                    v4i Dc[TM];
+                    Acc Dc[TM];
                     float2 dwc = make_float2(0.0f, 0.0f);
                     if (j < TN) {
-                        const long b = widen_q4_0(*reinterpret_cast<const uint32_t *>(W + (kc * BN + (wn * TN + j) * 16 + swc) * 16 + 4 * g));
-                        dwc = Dw[kc * BN + (wn * TN + j) * 16 + j16];
+                        const Op b = load_b(W, kc, (wn * TN + j) * MF + rc);
+                        dwc = Dw[kc * BN + (wn * TN + j) * MF + rc];
 #pragma unroll
                         for (int i = 0; i < TM; i++)
-                            Dc[i] = __builtin_amdgcn_mfma_i32_16x16x32_i8(a[i], b, magic, 0, 0, 0);
+                            Dc[i] = M::mma(a[i], b, magic);
                     }
                     if (j > 0) {
 #pragma unroll
                         for (int i = 0; i < TM; i++) {
-                            const float dq[4] = {da[i].x, da[i].y, da[i].z, da[i].w};
 #pragma unroll
-                            for (int r = 0; r < 4; r++) {
-                                const float t = __builtin_fmaf(__int_as_float(Dp[i][r]), dwp.x, dwp.y);
-                                acc[i][j - 1][r] = __builtin_fmaf(t, dq[r], acc[i][j - 1][r]);
+                            for (int q = 0; q < RG / 4; q++) {
+                                const float dq[4] = {da[i][q].x, da[i][q].y, da[i][q].z, da[i][q].w};
+#pragma unroll
+                                for (int e = 0; e < 4; e++) {
+                                    const int r = 4 * q + e;
+                                    const float t = __builtin_fmaf(__int_as_float(Dp[i][r]), dwp.x, dwp.y);
+                                    acc[i][j - 1][r] = __builtin_fmaf(t, dq[e], acc[i][j - 1][r]);
+                                }
                             }
                         }
                     }
@@ -451,17 +554,24 @@ __global__ __launch_bounds__(C::kThreads, C::kOcc) void w4a4_kernel(GemmProblem 
                 }
             }
         }
-
     };
+
+    const int nstages = (B + KC - 1) / KC;
+    if (KC <= B)
+        load_stage(0, std::true_type{});
+    else
+        load_stage(0, std::false_type{});
+    store_stage(lds);
+    __syncthreads();
 
     // Stages alternate between the two buffers; the loop is unrolled by two
     // so that every LDS address carries its buffer offset as an immediate.
-    for (int64_t s = 0; s < nstages; s += 2) {
+    for (int s = 0; s < nstages; s += 2) {
 #pragma unroll
         for (int half = 0; half < 2; half++) {
-            const int64_t st = s + half;
+            const int st = s + half;
             if (st < nstages) {
-                const int64_t kb0 = st * KC;
+                const int kb0 = st * KC;
                 const bool more = st + 1 < nstages;
                 if (more) {
                     if (kb0 + 2 * KC <= B)
@@ -493,23 +603,23 @@ __global__ __launch_bounds__(C::kThreads, C::kOcc) void w4a4_kernel(GemmProblem 
                 continue;
             const int i = t / TN, j = t % TN;
 #pragma unroll
-            for (int r = 0; r < 4; r++)
-                red[(((grp * WK + wk) * R + (t - t0)) * 4 + r) * 64 + lane] = acc[i][j][r];
+            for (int r = 0; r < RG; r++)
+                red[(((grp * WK + wk) * R + (t - t0)) * RG + r) * 64 + lane] = acc[i][j][r];
         }
         __syncthreads();
         for (int tt = wk; tt < R && t0 + tt < C::kTiles; tt += WK) {
             const int t = t0 + tt;
             const int i = t / TN, j = t % TN;
-            const int64_t col = col0 + (wn * TN + j) * 16 + j16;
+            const int64_t col = col0 + (wn * TN + j) * MF + rc;
 #pragma unroll
-            for (int r = 0; r < 4; r++) {
-                float v = red[(((grp * WK + 0) * R + tt) * 4 + r) * 64 + lane];
+            for (int r = 0; r < RG; r++) {
+                float v = red[(((grp * WK + 0) * R + tt) * RG + r) * 64 + lane];
 #pragma unroll
                 for (int w = 1; w < WK; w++)
-                    v += red[(((grp * WK + w) * R + tt) * 4 + r) * 64 + lane];
-                const int rl = 4 * g + r;
+                    v += red[(((grp * WK + w) * R + tt) * RG + r) * 64 + lane];
+                const int rl = M::out_row(g, r);
                 if (rl < vrows[i])
-                    p.y[(row0 + (wm * TM + i) * 16 + rl) * p.ldy + col] = v * unscale;
+                    p.y[(row0 + (wm * TM + i) * MF + rl) * p.ldy + col] = v * unscale;
             }
         }
         __syncthreads();
@@ -536,45 +646,43 @@ hipError_t launch_dense_cfg(const GemmProblem &p, hipStream_t stream)
     return launch_cfg<C, kGemm>(p, tm, tn, 0, 0, (int64_t)tm * tn, stream);
 }
 
-// Dense tile shapes.  Wide shapes run one 8-wave workgroup per CU whose
+// Dense tile shapes.  The wide shapes run one 8-wave workgroup per CU whose
 // waves advance together through the stage barriers (two independent
 // workgroups on one CU finish at different times: the older one gets issue
 // priority and the younger then runs alone).  KC = 8 blocks per stage.
 template <int BITS> struct Tiles {
-    // 64 x 160: two column halves of 64 x 80, K split in four (8-bit codes
-    // stage 4 blocks at a time to stay within 256 registers)
-    using W64x160 = Cfg<BITS, 4, 5, 1, 2, 4, BITS == 8 ? 4 : 8>;
-    // 64 x 128: two column halves of 64 x 64, K split in four
-    using W64x128 = Cfg<BITS, 4, 4, 1, 2, 4, 8>;
-    // 64 x 64: four waves, K split in four (two workgroups per CU)
-    using T64x64 = Cfg<BITS, 4, 4, 1, 1, 4, 8>;
-    using T64x32 = Cfg<BITS, 4, 2, 1, 1, 4, 8>;
+    // 64 x 160: two column halves of 64 x 80 (16x16 tiles), K split in four
+    // (8-bit codes stage 4 blocks at a time to stay within 256 registers)
+    using W64x160 = Cfg<BITS, 16, 4, 5, 1, 2, 4, BITS == 8 ? 4 : 8>;
+    // 64 x 128: two row halves of 32 x 128, K split in four
+    using W64x128 = Cfg<BITS, 32, 1, 4, 2, 1, 4, 8>;
+    // 64 x 64 and 64 x 32: four waves of 16x16 tiles, K split in four (two
+    // workgroups per CU)
+    using T64x64 = Cfg<BITS, 16, 4, 4, 1, 1, 4, 8>;
+    using T64x32 = Cfg<BITS, 16, 4, 2, 1, 1, 4, 8>;
     // small M: 16 rows, K split in four
-    using T16x64 = Cfg<BITS, 1, 4, 1, 1, 4, 8>;
-    using T16x32 = Cfg<BITS, 1, 2, 1, 1, 4, 8>;
+    using T16x64 = Cfg<BITS, 16, 1, 4, 1, 1, 4, 8>;
+    using T16x32 = Cfg<BITS, 16, 1, 2, 1, 1, 4, 8>;
 };
 
 constexpr int kCUs = 256;
 
-// Estimated time of a shape: rounds of resident workgroups times the
-// per-wave cost of one block (epilogue 8 per 16x16 tile, operand unpacking
-// 3 per row tile and 5 per column tile), divided by the waves per SIMD.
-inline double est(int64_t m, int64_t n, int bm, int bn, int tm, int tn, int per_cu,
-                  int waves_per_simd)
-{
-    if (n % bn != 0)
-        return 1e300;
-    const int64_t tiles = ((m + bm - 1) / bm) * (n / bn);
-    const int64_t slots = (int64_t)per_cu * kCUs;
-    const double rounds = (double)((tiles + slots - 1) / slots);
-    const double cost = 8.0 * tm * tn + 3.0 * tm + 5.0 * tn + 2.0 * tm * tn;
-    return rounds * cost * waves_per_simd;
-}
-
+// Estimated time of a shape: rounds of resident workgroups times the per-wave
+// issue cost of one block (two VALU per result register, operand unpacking
+// per row and column tile, matrix instruction issue per tile), times the
+// waves that share a SIMD.
 template <class C>
 double est_cfg(int64_t m, int64_t n)
 {
-    return est(m, n, C::BM, C::BN, C::TM, C::TN, C::kOcc, C::kWaves * C::kOcc / 4);
+    if (n % C::BN != 0)
+        return 1e300;
+    const int64_t tiles = ((m + C::BM - 1) / C::BM) * (n / C::BN);
+    const int64_t slots = (int64_t)C::kOcc * kCUs;
+    const double rounds = (double)((tiles + slots - 1) / slots);
+    const double wide = C::MF == 32 ? 2.0 : 1.0;
+    const double cost = 2.0 * C::kRegs * C::kTiles + wide * (3.0 * C::TM + 5.0 * C::TN) +
+                        2.0 * wide * C::kTiles;
+    return rounds * cost * (C::kWaves * C::kOcc / 4.0);
 }
 
 template <int BITS>
@@ -604,8 +712,8 @@ hipError_t launch_dense_bits(const GemmProblem &p, hipStream_t stream)
 template <int BITS>
 hipError_t launch_grouped_bits(const GemmProblem &p, hipStream_t stream)
 {
-    using C = Cfg<BITS, 2, 4, 1, 1, 4, 8>;  // 32 x 64
-    using C32 = Cfg<BITS, 2, 2, 1, 1, 4, 8>; // 32 x 32
+    using C = Cfg<BITS, 16, 2, 4, 1, 1, 4, 8>;   // 32 x 64
+    using C32 = Cfg<BITS, 16, 2, 2, 1, 1, 4, 8>; // 32 x 32
     // every expert needs ceil(rows_e / BM) slots: bounded by both of these
     int64_t slots = (p.rows + p.experts * (C::BM - 1)) / C::BM;
     if (slots > p.rows)
@@ -621,7 +729,8 @@ hipError_t launch_grouped_bits(const GemmProblem &p, hipStream_t stream)
 template <int BITS>
 hipError_t launch_sums_bits(const GemmProblem &p, hipStream_t stream)
 {
-    using C = Cfg<BITS, 2, 2, 1, 1, 4, 8>; // 32 x 32
+    // the 32x32 main loop of the wide dense shapes, one 32x32 tile per workgroup
+    using C = Cfg<BITS, 32, 1, 1, 1, 1, 4, 8>;
     const int tm0 = (int)(p.m0 / C::BM), tm1 = (int)((p.m1 + C::BM - 1) / C::BM);
     const int tn0 = (int)(p.n0 / C::BN), tn1 = (int)((p.n1 + C::BN - 1) / C::BN);
     const int tm = tm1 - tm0, tn = tn1 - tn0;
@@ -634,6 +743,8 @@ hipError_t launch_gemm(const GemmProblem &p, hipStream_t stream)
 {
     if (p.rows == 0)
         return hipSuccess;
+    if (skinny_fits(p))
+        return launch_skinny(p, stream);
     return p.act_bits == 4 ? launch_dense_bits<4>(p, stream) : launch_dense_bits<8>(p, stream);
 }
 

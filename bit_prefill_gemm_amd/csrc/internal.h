@@ -31,6 +31,10 @@ struct GemmProblem {
 };
 
 hipError_t launch_gemm(const GemmProblem &p, hipStream_t stream);
+// The weight-stream kernel for a few rows (dense only): usable when
+// skinny_fits(p).
+bool skinny_fits(const GemmProblem &p);
+hipError_t launch_skinny(const GemmProblem &p, hipStream_t stream);
 hipError_t launch_grouped_gemm(const GemmProblem &p, hipStream_t stream);
 hipError_t launch_blocksums(const GemmProblem &p, hipStream_t stream);
 

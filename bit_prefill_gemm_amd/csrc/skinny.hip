@@ -1,0 +1,335 @@
+// skinny.hip -- the W4A4 / W4A8 product for a few rows (M <= 32): a weight
+// stream (gfx950).
+//
+// "509 tokens a second of prompt: the Hadamard route ships", section "Why
+// prompts are a matrix-unit problem": with only a handful of rows every
+// weight byte is used for a few multiply-adds, so the product is bound by how
+// fast the Q4_0 weight image streams from HBM, not by the matrix unit.  This
+// kernel is shaped for that:
+//   - one workgroup per 32-column image tile; its NW waves split K into
+//     contiguous ranges of groups of four blocks, so every wave streams its
+//     own run of the tile (32 columns x 4 blocks x 18 bytes per group);
+//   - every load is 16 (or 8) bytes wide: the weight image interleaves four
+//     blocks, so one read per lane and 16-column tile holds that lane's
+//     matrix operands for the group's four blocks; an activation read holds
+//     one block of one row and a 4x4 transpose across the lane rows (gfx950
+//     permlane swaps) turns four of them into the operands of four blocks;
+//   - operands go straight from global memory into registers (no LDS
+//     staging, no barriers in the main loop), with D groups of loads in
+//     flight per wave while a group is computed;
+//   - the few activation rows are re-read from L2; their scales are staged
+//     once per workgroup in LDS, transposed, so the epilogue reads four rows'
+//     scales with one LDS read;
+//   - the partial sums of the waves are added in a fixed order (wave 0, 1,
+//     ...) through LDS, so the result is bit-identical from run to run.
+// The per-block arithmetic is the one of the tiled kernel: operands widened
+// to 16 x value, one v_mfma_i32_16x16x32_i8 per 16x16 tile and block with the
+// accumulator input 0x4B400000, then t = fma(F, dw, -12582912*dw) (exact) and
+// acc = fma(t, da, acc).  Rows past M repeat the last row; their sums reach
+// only outputs that are never stored.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "internal.h"
+
+namespace bpg {
+
+namespace {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+constexpr int kMagicBits = 0x4B400000;
+constexpr float kMagic = 12582912.0f;
+
+template <int BITS_, int TM_, int NW_>
+struct SkCfg {
+    static constexpr int BITS = BITS_, TM = TM_, NW = NW_;
+    static constexpr int TN = 2;                      // 16-column tiles per workgroup (one image tile)
+    static constexpr int D = 4;                       // groups of four blocks in flight per wave
+    static constexpr int kThreads = 64 * NW;
+    static constexpr int kRows = 16 * TM;             // rows covered (M <= kRows)
+    static constexpr int kAB = BITS == 4 ? 16 : 32;   // code bytes per (row, block)
+    static constexpr int kAH = kAB / 16;              // 16-byte halves per (row, block)
+    static constexpr int kShift = BITS == 4 ? 8 : 4;  // log2 of the operand widening
+    static constexpr int kR = TM * TN * 4;            // accumulators per lane
+    static constexpr int kLdsRed = NW * kR * 64 * 4;  // bytes for the final reduction
+};
+
+__device__ __forceinline__ uint32_t act_lo(uint32_t d) { return (d << 4) & 0xF0F0F0F0u; }
+__device__ __forceinline__ uint32_t act_hi(uint32_t d) { return d & 0xF0F0F0F0u; }
+__device__ __forceinline__ uint32_t q40_lo(uint32_t d) { return ((d << 4) ^ 0x80808080u) & 0xF0F0F0F0u; }
+__device__ __forceinline__ uint32_t q40_hi(uint32_t d) { return (d ^ 0x88888888u) & 0xF0F0F0F0u; }
+
+__device__ __forceinline__ long pack2(uint32_t lo, uint32_t hi)
+{
+    return (long)(((uint64_t)hi << 32) | lo);
+}
+
+// The same address in every lane, made visibly uniform (scalar registers).
+typedef const __attribute__((address_space(1))) uint8_t *gptr;
+
+__device__ __forceinline__ gptr uniform_ptr(const void *p)
+{
+    const uint64_t a = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
+    return (gptr)(((uint64_t)hi << 32) | lo);
+}
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint4 gload16(gptr base, uint32_t off)
+{
+    const u32x4 v = *(const __attribute__((address_space(1))) u32x4 *)(base + off);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ uint2 gload8(gptr base, uint32_t off)
+{
+    const u32x2 v = *(const __attribute__((address_space(1))) u32x2 *)(base + off);
+    return make_uint2(v.x, v.y);
+}
+
+// 4x4 transpose across the four 16-lane rows of a wave: on entry register q
+// of row g holds element (g, q); on exit it holds element (q, g).  Two
+// 32-lane swaps exchange the off-diagonal 2x2 quadrants, two 16-lane swaps
+// the off-diagonal elements inside each quadrant.
+__device__ __forceinline__ void transpose_rows4(uint4 &v)
+{
+    auto a = __builtin_amdgcn_permlane32_swap(v.x, v.z, false, false);
+    auto b = __builtin_amdgcn_permlane32_swap(v.y, v.w, false, false);
+    auto c = __builtin_amdgcn_permlane16_swap(a[0], b[0], false, false);
+    auto d = __builtin_amdgcn_permlane16_swap(a[1], b[1], false, false);
+    v = make_uint4(c[0], c[1], d[0], d[1]);
+}
+
+template <class C>
+__global__ __launch_bounds__(C::kThreads) void skinny_kernel(GemmProblem p)
+{
+    constexpr int TM = C::TM, TN = C::TN, D = C::D, NW = C::NW, NT = C::kThreads;
+    constexpr int kRows = C::kRows, kAB = C::kAB, kAH = C::kAH, R = C::kR;
+    extern __shared__ __attribute__((aligned(16))) float lds[];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int c = lane & 15; // operand row / column inside a 16x16 tile
+    const int g = lane >> 4; // operand K group (dword g of a block); result row group
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int B = (int)(p.k / 32); // the host limits K
+    const int NG = (B + 3) / 4;    // groups of four blocks
+    const int rows = (int)p.rows;  // 1 .. kRows
+    const int64_t tile = blockIdx.x;
+    const int64_t col0 = tile * 32;
+
+    // ---- activation scales, transposed to [block][row] (zero past M)
+    float *Da = lds;
+    for (int idx = tid; idx < B * kRows; idx += NT) {
+        const int m = idx / B, b = idx - m * B;
+        Da[b * kRows + m] = m < rows ? p.scales[(int64_t)m * B + b] : 0.0f;
+    }
+
+    // ---- this wave's groups and its operand offsets.  Per group and lane:
+    //      weights: one 16-byte read per 16-column tile = slot g of column c
+    //      for the group's four blocks (the image interleaves them so);
+    //      scales: 8 bytes = the four blocks' scales of column c;
+    //      activations: 16 bytes = block 4G+g of row c, turned by a 4x4
+    //      transpose across the lane rows into slot g of the four blocks.
+    const int g0 = (int)((int64_t)wave * NG / NW);
+    const int g1 = (int)((int64_t)(wave + 1) * NG / NW);
+    const int64_t arow = p.k * kAB / 32;
+    const gptr a_base = uniform_ptr(p.codes);
+    const gptr w_base = uniform_ptr(p.wcodes + tile * NG * 2048);
+    const gptr dw_base = uniform_ptr(p.wscales + tile * NG * 128);
+    uint32_t va[TM], vw[TN], vdw[TN];
+#pragma unroll
+    for (int i = 0; i < TM; i++) {
+        const int m = 16 * i + c;
+        va[i] = (uint32_t)((m < rows ? m : rows - 1) * arow);
+    }
+#pragma unroll
+    for (int j = 0; j < TN; j++) {
+        vw[j] = (uint32_t)((g * 32 + 16 * j + c) * 16);
+        vdw[j] = (uint32_t)((16 * j + c) * 8);
+    }
+
+    // ring of D groups of operands in registers
+    uint4 rw[D][TN], ra[D][TM][kAH];
+    uint2 rdw[D][TN];
+    auto load = [&](int d, int G) {
+        const gptr wb = w_base + G * 2048, dwb = dw_base + G * 256;
+        // the last group may end past block B-1: those lanes re-read block B-1
+        const int bq = min(4 * G + g, B - 1);
+#pragma unroll
+        for (int j = 0; j < TN; j++) {
+            rw[d][j] = gload16(wb, vw[j]);
+            rdw[d][j] = gload8(dwb, vdw[j]);
+        }
+#pragma unroll
+        for (int i = 0; i < TM; i++)
+#pragma unroll
+            for (int h = 0; h < kAH; h++)
+                ra[d][i][h] = gload16(a_base, va[i] + bq * kAB + 16 * h);
+    };
+
+    float acc[TM][TN][4];
+#pragma unroll
+    for (int i = 0; i < TM; i++)
+#pragma unroll
+        for (int j = 0; j < TN; j++)
+#pragma unroll
+            for (int r = 0; r < 4; r++)
+                acc[i][j][r] = 0.0f;
+    v4i magic;
+#pragma unroll
+    for (int r = 0; r < 4; r++)
+        magic[r] = kMagicBits;
+
+    auto compute = [&](int d, int G) {
+#pragma unroll
+        for (int i = 0; i < TM; i++)
+#pragma unroll
+            for (int h = 0; h < kAH; h++)
+                transpose_rows4(ra[d][i][h]);
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+            const int b = 4 * G + q;
+            if (b >= B)
+                break; // uniform
+            long a[TM];
+            float4 da[TM];
+#pragma unroll
+            for (int i = 0; i < TM; i++) {
+                const uint32_t lo = q == 0 ? ra[d][i][0].x : q == 1 ? ra[d][i][0].y
+                                  : q == 2 ? ra[d][i][0].z : ra[d][i][0].w;
+                const uint32_t hi = q == 0 ? ra[d][i][kAH - 1].x : q == 1 ? ra[d][i][kAH - 1].y
+                                  : q == 2 ? ra[d][i][kAH - 1].z : ra[d][i][kAH - 1].w;
+                // 4-bit: low and high nibbles of dword g; 8-bit: bytes 4g.. and 16+4g..
+                a[i] = kAH == 1 ? pack2(act_lo(lo), act_hi(lo)) : pack2(lo, hi);
+                da[i] = *reinterpret_cast<const float4 *>(Da + b * kRows + 16 * i + 4 * g);
+            }
+#pragma unroll
+            for (int j = 0; j < TN; j++) {
+                const uint32_t wd = q == 0 ? rw[d][j].x : q == 1 ? rw[d][j].y
+                                  : q == 2 ? rw[d][j].z : rw[d][j].w;
+                const long w = pack2(q40_lo(wd), q40_hi(wd));
+                const uint32_t hp = q < 2 ? rdw[d][j].x : rdw[d][j].y;
+                const uint16_t hb = (uint16_t)((q & 1) ? hp >> 16 : hp & 0xFFFFu);
+                const float dw = (float)__builtin_bit_cast(_Float16, hb);
+                const float cm = -kMagic * dw; // exact: dw has 11 significant bits
+#pragma unroll
+                for (int i = 0; i < TM; i++) {
+                    const v4i s = __builtin_amdgcn_mfma_i32_16x16x32_i8(a[i], w, magic, 0, 0, 0);
+                    const float dq[4] = {da[i].x, da[i].y, da[i].z, da[i].w};
+#pragma unroll
+                    for (int r = 0; r < 4; r++) {
+                        const float t = __builtin_fmaf(__int_as_float(s[r]), dw, cm);
+                        acc[i][j][r] = __builtin_fmaf(t, dq[r], acc[i][j][r]);
+                    }
+                }
+            }
+        }
+    };
+
+    // Every slot is refilled right after its group is computed, so D groups
+    // of loads are always in flight.  The loads are unconditional (groups past
+    // the wave's range re-read its last group and are never computed), which
+    // keeps the order of outstanding loads the same in every iteration; the
+    // scheduling barriers keep the prologue's loads in that same slot order.
+    const int last = g1 > g0 ? g1 - 1 : g0;
+#pragma unroll
+    for (int d = 0; d < D; d++) {
+        load(d, min(g0 + d, last));
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    __syncthreads(); // the scales in LDS
+
+    for (int base = g0; base < g1; base += D) {
+#pragma unroll
+        for (int d = 0; d < D; d++) {
+            const int G = base + d;
+            if (G < g1)
+                compute(d, G);
+            load(d, min(G + D, last));
+        }
+    }
+
+    // ---- fixed-order sum over the waves (wave 0, 1, ...); widening removed
+    __syncthreads(); // every wave is done with the scales
+    float *red = lds;
+#pragma unroll
+    for (int i = 0; i < TM; i++)
+#pragma unroll
+        for (int j = 0; j < TN; j++)
+#pragma unroll
+            for (int r = 0; r < 4; r++)
+                red[(wave * R + (i * TN + j) * 4 + r) * 64 + lane] = acc[i][j][r];
+    __syncthreads();
+    const float unscale = 1.0f / (float)(1 << C::kShift);
+    for (int v = tid; v < R * 64; v += NT) {
+        float s = red[v];
+#pragma unroll
+        for (int w = 1; w < NW; w++)
+            s += red[w * R * 64 + v];
+        const int q = v >> 6, ln = v & 63;
+        const int i = q / (TN * 4), j = (q / 4) % TN, r = q % 4;
+        const int m = 16 * i + 4 * (ln >> 4) + r;
+        if (m < rows)
+            p.y[(int64_t)m * p.ldy + col0 + 16 * j + (ln & 15)] = s * unscale;
+    }
+}
+
+template <class C>
+size_t skinny_lds(const GemmProblem &p)
+{
+    const size_t da = (size_t)(p.k / 32) * C::kRows * 4;
+    return da > (size_t)C::kLdsRed ? da : (size_t)C::kLdsRed;
+}
+
+template <class C>
+hipError_t launch_cfg(const GemmProblem &p, hipStream_t stream)
+{
+    const size_t lds = skinny_lds<C>(p);
+    skinny_kernel<C><<<dim3((unsigned)(p.n / 32)), C::kThreads, lds, stream>>>(p);
+    return hipGetLastError();
+}
+
+// Waves per workgroup: enough waves in the whole grid to keep the weight
+// stream busy (about 8 per CU), each with at least D groups of K.
+template <int BITS, int TM>
+hipError_t launch_tm(const GemmProblem &p, hipStream_t stream)
+{
+    const int64_t tiles = p.n / 32, NG = (p.k / 32 + 3) / 4;
+    // (two row tiles need more registers: at most 8 waves, 2 per SIMD)
+    const int nw_max = TM == 1 ? 16 : 8;
+    int nw = 4;
+    while (nw < nw_max && tiles * nw < 2048 && NG / (2 * nw) >= 4)
+        nw *= 2;
+    if (nw == 4)
+        return launch_cfg<SkCfg<BITS, TM, 4>>(p, stream);
+    if constexpr (TM == 1) {
+        if (nw == 16)
+            return launch_cfg<SkCfg<BITS, TM, 16>>(p, stream);
+    }
+    return launch_cfg<SkCfg<BITS, TM, 8>>(p, stream);
+}
+
+} // namespace
+
+bool skinny_fits(const GemmProblem &p)
+{
+    if (p.rows < 1 || p.rows > 32)
+        return false;
+    const int rows_cov = p.rows <= 16 ? 16 : 32;
+    // the transposed scales must fit the 64 KB of dynamic LDS
+    return (p.k / 32) * rows_cov * 4 <= 65536;
+}
+
+hipError_t launch_skinny(const GemmProblem &p, hipStream_t stream)
+{
+    if (p.act_bits == 4)
+        return p.rows <= 16 ? launch_tm<4, 1>(p, stream) : launch_tm<4, 2>(p, stream);
+    return p.rows <= 16 ? launch_tm<8, 1>(p, stream) : launch_tm<8, 2>(p, stream);
+}
+
+} // namespace bpg

@@ -79,25 +79,31 @@ typedef enum { BPG_X_F32 = 0, BPG_X_BF16 = 1 } bpg_x_dtype;
 
 #define BPG_WEIGHTS_MAGIC 0x57475042u /* "BPGW" little-endian */
 #define BPG_WEIGHTS_VERSION 1u
-#define BPG_LAYOUT_COLTILE32 1u
+#define BPG_LAYOUT_COLTILE32_K4 2u
 
 /*
  * Stamp of a packed weight image (the analogue of the rotated file's stamp:
  * a GEMM refuses an image whose stamp is missing or does not say rotated).
  *
- * Device image, layout BPG_LAYOUT_COLTILE32, for E experts (1 if dense),
- * B = K/32 blocks per row and N/32 column tiles:
- *   codes  at byte 0:           [E][N/32][B][32 columns][16 B]   the 16 Q4_0
- *          nibble bytes of block (n, b) verbatim (byte j: element j in the low
- *          nibble, element j+16 in the high nibble; code u means u-8);
- *   scales at scales_offset:    [E][N/32][B][32 columns] fp16, the block scale.
- * Total bytes = E*N*K*18/32, as for Q4_0.
+ * Device image, layout BPG_LAYOUT_COLTILE32_K4, for E experts (1 if dense),
+ * B = K/32 blocks per row, G = ceil(B/4) groups of four blocks and T = N/32
+ * column tiles of 32 columns:
+ *   codes  at byte 0:           uint32 [E][T][G][4 slots s][32 columns][4 blocks q]:
+ *          dword s (bytes 4s..4s+3) of the 16 Q4_0 nibble bytes of column
+ *          32t+c, block 4G+q (byte j: element j in the low nibble, element
+ *          j+16 in the high nibble; code u means u-8);
+ *   scales at scales_offset:    fp16 [E][T][G][32 columns][4 blocks q], the
+ *          block scale.
+ * Blocks past B (when B is not a multiple of 4) hold codes 0x88 (value 0)
+ * and scale 0.  One 16-byte read at (t, G, s, c) holds slot s of column c for
+ * four consecutive blocks.  Total bytes = E*T*G*2304 (= E*N*K*18/32, as for
+ * Q4_0, when K is a multiple of 128).
  */
 typedef struct {
     uint32_t magic;        /* BPG_WEIGHTS_MAGIC */
     uint32_t version;      /* BPG_WEIGHTS_VERSION */
     uint32_t rotation;     /* 32: every block rotated by H32 */
-    uint32_t layout;       /* BPG_LAYOUT_COLTILE32 */
+    uint32_t layout;       /* BPG_LAYOUT_COLTILE32_K4 */
     int64_t n;             /* output channels per expert */
     int64_t k;             /* input channels */
     int64_t num_experts;   /* 1 for a dense weight */

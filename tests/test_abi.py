@@ -47,10 +47,11 @@ def test_status_strings():
 
 def good_desc(n=64, k=128, e=1):
     d = bb.WeightsDesc()
-    d.magic, d.version, d.rotation, d.layout = 0x57475042, 1, 32, 1
+    d.magic, d.version, d.rotation, d.layout = 0x57475042, 1, 32, 2
     d.n, d.k, d.num_experts = n, k, e
-    d.bytes = e * n * (k // 32) * 18
-    d.scales_offset = e * n * (k // 32) * 16
+    groups = (k // 32 + 3) // 4
+    d.bytes = e * (n // 32) * groups * 2304
+    d.scales_offset = e * (n // 32) * groups * 2048
     return d
 
 
@@ -101,6 +102,7 @@ def _desc_with(**kw):
     (dict(desc=_desc_with(rotation=0)), STAMP),      # an unrotated image is refused
     (dict(desc=_desc_with(rotation=64)), STAMP),
     (dict(desc=_desc_with(layout=0)), STAMP),
+    (dict(desc=_desc_with(layout=1)), STAMP),        # the earlier, non-interleaved layout
     (dict(desc=_desc_with(bytes=1)), STAMP),
     (dict(desc=_desc_with(scales_offset=8)), STAMP),
     (dict(desc=_desc_with(n=48)), STAMP),
@@ -159,6 +161,7 @@ def test_pack_errors():
     assert lib.rotate_pack_weights(sp, 2, 64, 128, 1, dp, dst.nbytes - 1, ctypes.byref(d)) == BUFFER
     assert lib.rotate_pack_weights(sp, 2, 64, 128, 1, dp, dst.nbytes, ctypes.byref(d)) == OK
     assert lib.rotate_pack_weights_bytes(64, 128, 1) == 64 * 4 * 18
+    assert lib.rotate_pack_weights_bytes(64, 160, 1) == 2 * 2 * 2304   # two groups, three pad blocks
     assert lib.rotate_pack_weights_bytes(63, 128, 1) == 0
     assert lib.rotate_pack_weights_bytes(64, 128, -1) == 0
 

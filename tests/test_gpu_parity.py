@@ -163,6 +163,39 @@ def test_gemm_ragged_shapes(torch, m, k, n, bits):
     check_gemm(case["x"], case["w"], n, k, bits, label="ragged")
 
 
+@pytest.mark.parametrize("m", [1, 7, 16, 17, 32])
+@pytest.mark.parametrize("k,n", [(32, 32), (1056, 96)])
+@pytest.mark.parametrize("bits", [4, 8])
+def test_gemm_few_rows(torch, m, k, n, bits):
+    """M <= 32 runs the weight-stream kernel: one and two row tiles, K shorter
+    than one block per wave and K not a multiple of the blocks in flight."""
+    case = synth.small_dense(m, k, n, seed=3 * m + k + n + bits)
+    check_gemm(case["x"], case["w"], n, k, bits, label="few rows")
+
+
+@pytest.mark.parametrize("k", [32768, 32800])
+def test_gemm_few_rows_long_k(torch, k):
+    """The largest K whose transposed row scales fit the weight-stream kernel's
+    LDS (1024 blocks for 16 rows), and one block more (the tiled kernel)."""
+    case = synth.small_dense(16, k, 64, seed=k)
+    check_gemm(case["x"], case["w"], 64, k, 4, label="few rows long K")
+
+
+def test_gemm_few_rows_output_stride(torch):
+    case = synth.small_dense(20, 160, 96, seed=5)
+    codes, scales, q, d = quantize_and_check(case["x"], 8)
+    W = weights_to_device(case["w"], 96, 160)
+    ybig = torch.full((20, 132), -1.0, device="cuda")
+    y = ybig[:, 8:104]
+    bb.w4a4_gemm(codes, scales, 8, W, y=y)
+    torch.cuda.synchronize()
+    yb = ybig.cpu().numpy()
+    assert np.all(yb[:, :8] == -1.0) and np.all(yb[:, 104:] == -1.0)
+    w, dw = oracle.q4_0_decode(case["w"], 160)
+    ref = oracle.gemm_rect(q, d, w, dw, 0, 20, 0, 96)
+    assert row_rel_err(yb[:, 8:104], ref) <= TIGHT
+
+
 def test_gemm_m0_is_noop(torch):
     case = synth.small_dense(4, 64, 32, seed=1)
     W = weights_to_device(case["w"], 32, 64)
@@ -205,11 +238,12 @@ def test_gemm_ffn512_full_size(torch):
     check_gemm(t["x2"], t["w_down"], 5120, 17408, 4, rows=rows, label="ffn down")
 
 
-@pytest.mark.parametrize("name", ["m16_gate", "m16_down", "m16_attn"])
-def test_gemm_m16_full_size(torch, name):
+@pytest.mark.parametrize("name,bits", [("m16_gate", 4), ("m16_down", 4), ("m16_attn", 4),
+                                       ("m16_attn", 8)])
+def test_gemm_m16_full_size(torch, name, bits):
     t = synth.make(name)
     c = t["cfg"]
-    check_gemm(t["x"], t["w"], c["n"], c["k"], 4, label=name)
+    check_gemm(t["x"], t["w"], c["n"], c["k"], bits, label=name)
 
 
 def test_long1024_routes_and_error_vs_unquantized(torch):

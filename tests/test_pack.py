@@ -8,21 +8,44 @@ from bit_prefill_gemm_amd import binding as bb
 from bit_prefill_gemm_amd import synth
 
 
+def image_regions(img: np.ndarray, n: int, k: int, e: int):
+    """The documented regions: codes uint32 [e][n/32][G][4 slots][32 cols][4 blocks],
+    scales fp16 bits [e][n/32][G][32 cols][4 blocks], G = ceil(k/128)."""
+    B = k // 32
+    G, T = (B + 3) // 4, n // 32
+    assert img.size == e * T * G * 2304
+    codes = img[: e * T * G * 2048].view("<u4").reshape(e, T, G, 4, 32, 4)
+    scales = img[e * T * G * 2048:].view("<u2").reshape(e, T, G, 32, 4)
+    return codes, scales
+
+
 def unpack_image(img: np.ndarray, n: int, k: int, e: int) -> np.ndarray:
     """Read the image back per its documented layout into canonical blocks [e, n, k/32, 18]."""
     B = k // 32
-    codes = img[: e * n * B * 16].reshape(e, n // 32, B, 32, 16)
-    scales = img[e * n * B * 16:].view("<u2").reshape(e, n // 32, B, 32)
+    codes, scales = image_regions(img, n, k, e)
     out = np.empty((e, n, B, 18), dtype=np.uint8)
-    for t in range(n // 32):
-        for j in range(32):
-            out[:, t * 32 + j, :, 2:] = codes[:, t, :, j, :]
-            out[:, t * 32 + j, :, 0:2] = scales[:, t, :, j].astype("<u2").view(np.uint8).reshape(
-                e, B, 2)
+    for b in range(B):
+        gi, q = divmod(b, 4)
+        d = np.ascontiguousarray(codes[:, :, gi, :, :, q].transpose(0, 1, 3, 2))  # [e][t][c][slot]
+        out[:, :, b, 2:] = d.view(np.uint8).reshape(e, n, 16)
+        sc = np.ascontiguousarray(scales[:, :, gi, :, q]).reshape(e, n)
+        out[:, :, b, 0:2] = sc.view(np.uint8).reshape(e, n, 2)
     return out
 
 
-@pytest.mark.parametrize("n,k,e", [(32, 32, 1), (96, 160, 1), (64, 256, 3)])
+def test_blocks_past_k_are_zero_valued():
+    """K = 160 (5 blocks): the second group's last three blocks are padding,
+    codes 0x88 (u = 8, value 0) and scale 0."""
+    n, k = 64, 160
+    blocks = synth.draw_q4_0(np.random.default_rng(7), (n,), k, 0.002, 0.02)
+    W = bb.rotate_pack_weights(blocks, bb.SRC_Q4_0_ROTATED, n, k, 1)
+    codes, scales = image_regions(W.image, n, k, 1)
+    pad_codes = codes[:, :, 1, :, :, 1:]
+    assert np.all(pad_codes == 0x88888888)
+    assert np.all(scales[:, :, 1, :, 1:] == 0)
+
+
+@pytest.mark.parametrize("n,k,e", [(32, 32, 1), (96, 160, 1), (64, 256, 3), (32, 416, 2)])
 def test_q4_0_source_is_relaid_out_verbatim(n, k, e):
     blocks = synth.draw_q4_0(np.random.default_rng(n + k + e), (e, n), k, 0.002, 0.02)
     W = bb.rotate_pack_weights(blocks, bb.SRC_Q4_0_ROTATED, n, k, e)
