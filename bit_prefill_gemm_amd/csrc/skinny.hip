@@ -41,11 +41,16 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 constexpr int kMagicBits = 0x4B400000;
 constexpr float kMagic = 12582912.0f;
 
-template <int BITS_, int TM_, int NW_>
+template <int BITS_, int TM_, int NW_, int TN_>
 struct SkCfg {
     static constexpr int BITS = BITS_, TM = TM_, NW = NW_;
-    static constexpr int TN = 2;                      // 16-column tiles per workgroup (one image tile)
-    static constexpr int D = 4;                       // groups of four blocks in flight per wave
+    static constexpr int TN = TN_;                    // 16-column tiles per workgroup (2: one image tile)
+    static constexpr int kCols = 16 * TN;
+    // groups of four blocks in flight per wave: one.  Deeper rings measured
+    // slower: with every wave of the grid streaming, more outstanding reads
+    // only lengthen the memory queues (the waves of a SIMD still overlap one
+    // another's waits).
+    static constexpr int D = 1;
     static constexpr int kThreads = 64 * NW;
     static constexpr int kRows = 16 * TM;             // rows covered (M <= kRows)
     static constexpr int kAB = BITS == 4 ? 16 : 32;   // code bytes per (row, block)
@@ -120,14 +125,9 @@ __global__ __launch_bounds__(C::kThreads) void skinny_kernel(GemmProblem p)
     const int NG = (B + 3) / 4;    // groups of four blocks
     const int rows = (int)p.rows;  // 1 .. kRows
     const int64_t tile = blockIdx.x;
-    const int64_t col0 = tile * 32;
+    const int64_t col0 = tile * C::kCols;
 
-    // ---- activation scales, transposed to [block][row] (zero past M)
     float *Da = lds;
-    for (int idx = tid; idx < B * kRows; idx += NT) {
-        const int m = idx / B, b = idx - m * B;
-        Da[b * kRows + m] = m < rows ? p.scales[(int64_t)m * B + b] : 0.0f;
-    }
 
     // ---- this wave's groups and its operand offsets.  Per group and lane:
     //      weights: one 16-byte read per 16-column tile = slot g of column c
@@ -139,8 +139,8 @@ __global__ __launch_bounds__(C::kThreads) void skinny_kernel(GemmProblem p)
     const int g1 = (int)((int64_t)(wave + 1) * NG / NW);
     const int64_t arow = p.k * kAB / 32;
     const gptr a_base = uniform_ptr(p.codes);
-    const gptr w_base = uniform_ptr(p.wcodes + tile * NG * 2048);
-    const gptr dw_base = uniform_ptr(p.wscales + tile * NG * 128);
+    const gptr w_base = uniform_ptr(p.wcodes + (col0 / 32) * NG * 2048);
+    const gptr dw_base = uniform_ptr(p.wscales + (col0 / 32) * NG * 128);
     uint32_t va[TM], vw[TN], vdw[TN];
 #pragma unroll
     for (int i = 0; i < TM; i++) {
@@ -149,8 +149,9 @@ __global__ __launch_bounds__(C::kThreads) void skinny_kernel(GemmProblem p)
     }
 #pragma unroll
     for (int j = 0; j < TN; j++) {
-        vw[j] = (uint32_t)((g * 32 + 16 * j + c) * 16);
-        vdw[j] = (uint32_t)((16 * j + c) * 8);
+        // 16-column tile j is half j % 2 of image tile j / 2
+        vw[j] = (uint32_t)((j / 2) * NG * 2048 + (g * 32 + 16 * (j % 2) + c) * 16);
+        vdw[j] = (uint32_t)((j / 2) * NG * 256 + (16 * (j % 2) + c) * 8);
     }
 
     // ring of D groups of operands in registers
@@ -185,19 +186,20 @@ __global__ __launch_bounds__(C::kThreads) void skinny_kernel(GemmProblem p)
     for (int r = 0; r < 4; r++)
         magic[r] = kMagicBits;
 
+    // One group: the matrix products of its four blocks first, then their
+    // epilogues, so that no result is read right after its instruction.  The
+    // last group may hold blocks past B: the image gives them scale 0 and LDS
+    // row scale 0, so they add exactly zero.
     auto compute = [&](int d, int G) {
 #pragma unroll
         for (int i = 0; i < TM; i++)
 #pragma unroll
             for (int h = 0; h < kAH; h++)
                 transpose_rows4(ra[d][i][h]);
+        v4i s[4][TN][TM];
 #pragma unroll
         for (int q = 0; q < 4; q++) {
-            const int b = 4 * G + q;
-            if (b >= B)
-                break; // uniform
             long a[TM];
-            float4 da[TM];
 #pragma unroll
             for (int i = 0; i < TM; i++) {
                 const uint32_t lo = q == 0 ? ra[d][i][0].x : q == 1 ? ra[d][i][0].y
@@ -206,24 +208,36 @@ __global__ __launch_bounds__(C::kThreads) void skinny_kernel(GemmProblem p)
                                   : q == 2 ? ra[d][i][kAH - 1].z : ra[d][i][kAH - 1].w;
                 // 4-bit: low and high nibbles of dword g; 8-bit: bytes 4g.. and 16+4g..
                 a[i] = kAH == 1 ? pack2(act_lo(lo), act_hi(lo)) : pack2(lo, hi);
-                da[i] = *reinterpret_cast<const float4 *>(Da + b * kRows + 16 * i + 4 * g);
             }
 #pragma unroll
             for (int j = 0; j < TN; j++) {
                 const uint32_t wd = q == 0 ? rw[d][j].x : q == 1 ? rw[d][j].y
                                   : q == 2 ? rw[d][j].z : rw[d][j].w;
                 const long w = pack2(q40_lo(wd), q40_hi(wd));
+#pragma unroll
+                for (int i = 0; i < TM; i++)
+                    s[q][j][i] = __builtin_amdgcn_mfma_i32_16x16x32_i8(a[i], w, magic, 0, 0, 0);
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+            const int b = 4 * G + q;
+            float4 da[TM];
+#pragma unroll
+            for (int i = 0; i < TM; i++)
+                da[i] = *reinterpret_cast<const float4 *>(Da + b * kRows + 16 * i + 4 * g);
+#pragma unroll
+            for (int j = 0; j < TN; j++) {
                 const uint32_t hp = q < 2 ? rdw[d][j].x : rdw[d][j].y;
                 const uint16_t hb = (uint16_t)((q & 1) ? hp >> 16 : hp & 0xFFFFu);
                 const float dw = (float)__builtin_bit_cast(_Float16, hb);
                 const float cm = -kMagic * dw; // exact: dw has 11 significant bits
 #pragma unroll
                 for (int i = 0; i < TM; i++) {
-                    const v4i s = __builtin_amdgcn_mfma_i32_16x16x32_i8(a[i], w, magic, 0, 0, 0);
                     const float dq[4] = {da[i].x, da[i].y, da[i].z, da[i].w};
 #pragma unroll
                     for (int r = 0; r < 4; r++) {
-                        const float t = __builtin_fmaf(__int_as_float(s[r]), dw, cm);
+                        const float t = __builtin_fmaf(__int_as_float(s[q][j][i][r]), dw, cm);
                         acc[i][j][r] = __builtin_fmaf(t, dq[r], acc[i][j][r]);
                     }
                 }
@@ -236,21 +250,64 @@ __global__ __launch_bounds__(C::kThreads) void skinny_kernel(GemmProblem p)
     // the wave's range re-read its last group and are never computed), which
     // keeps the order of outstanding loads the same in every iteration; the
     // scheduling barriers keep the prologue's loads in that same slot order.
-    const int last = g1 > g0 ? g1 - 1 : g0;
+    // Activation scales, transposed to [block][row]; zero past M and for the
+    // blocks of the last group past B.  The first kDaU per thread are loaded
+    // before the operand prologue and stored behind it, so both latencies
+    // overlap.
+    constexpr int kDaU = NW >= 16 ? 8 : 16;
+    const int da_total = 4 * NG * kRows;
+    float dv[kDaU];
+    auto da_load = [&](int base) {
+#pragma unroll
+        for (int u = 0; u < kDaU; u++) {
+            const int idx = base + u * NT;
+            const int m = idx / (4 * NG), b = idx - m * (4 * NG);
+            dv[u] = idx < da_total && m < rows && b < B ? p.scales[(int64_t)m * B + b] : 0.0f;
+        }
+    };
+    auto da_store = [&](int base) {
+#pragma unroll
+        for (int u = 0; u < kDaU; u++) {
+            const int idx = base + u * NT;
+            const int m = idx / (4 * NG), b = idx - m * (4 * NG);
+            if (idx < da_total)
+                Da[b * kRows + m] = dv[u];
+        }
+    };
+    da_load(tid);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // The wave walks its groups starting at an offset that depends on the
+    // tile, so that the workgroups of different tiles, which all read the
+    // same few activation rows, do not read the same lines at the same time.
+    const int ng = g1 - g0;
+    const int rot = ng > 0 ? (int)(tile % ng) : 0;
+    auto group_at = [&](int k) { // k-th group of the walk; clamped to the last one
+        if (ng <= 0)
+            return min(g0, NG - 1);
+        const int r = min(k, ng - 1) + rot;
+        return g0 + (r >= ng ? r - ng : r);
+    };
 #pragma unroll
     for (int d = 0; d < D; d++) {
-        load(d, min(g0 + d, last));
+        load(d, group_at(d));
         __builtin_amdgcn_sched_barrier(0);
+    }
+
+    da_store(tid);
+    for (int base = tid + kDaU * NT; base < da_total; base += kDaU * NT) {
+        da_load(base);
+        da_store(base);
     }
     __syncthreads(); // the scales in LDS
 
-    for (int base = g0; base < g1; base += D) {
+    for (int base = 0; base < ng; base += D) {
 #pragma unroll
         for (int d = 0; d < D; d++) {
-            const int G = base + d;
-            if (G < g1)
-                compute(d, G);
-            load(d, min(G + D, last));
+            const int k = base + d;
+            if (k < ng)
+                compute(d, group_at(k));
+            load(d, group_at(k + D));
         }
     }
 
@@ -282,7 +339,7 @@ __global__ __launch_bounds__(C::kThreads) void skinny_kernel(GemmProblem p)
 template <class C>
 size_t skinny_lds(const GemmProblem &p)
 {
-    const size_t da = (size_t)(p.k / 32) * C::kRows * 4;
+    const size_t da = (size_t)((p.k / 32 + 3) / 4) * 4 * C::kRows * 4;
     return da > (size_t)C::kLdsRed ? da : (size_t)C::kLdsRed;
 }
 
@@ -290,28 +347,34 @@ template <class C>
 hipError_t launch_cfg(const GemmProblem &p, hipStream_t stream)
 {
     const size_t lds = skinny_lds<C>(p);
-    skinny_kernel<C><<<dim3((unsigned)(p.n / 32)), C::kThreads, lds, stream>>>(p);
+    skinny_kernel<C><<<dim3((unsigned)(p.n / C::kCols)), C::kThreads, lds, stream>>>(p);
     return hipGetLastError();
 }
 
 // Waves per workgroup: enough waves in the whole grid to keep the weight
-// stream busy (about 8 per CU), each with at least D groups of K.
-template <int BITS, int TM>
-hipError_t launch_tm(const GemmProblem &p, hipStream_t stream)
+// stream busy (about 8 per CU), each with at least 4 groups of K.
+template <int BITS, int TM, int TN>
+hipError_t launch_tn(const GemmProblem &p, hipStream_t stream)
 {
-    const int64_t tiles = p.n / 32, NG = (p.k / 32 + 3) / 4;
-    // (two row tiles need more registers: at most 8 waves, 2 per SIMD)
-    const int nw_max = TM == 1 ? 16 : 8;
+    const int64_t tiles = p.n / (16 * TN), NG = (p.k / 32 + 3) / 4;
+    // (two row tiles need more registers: at most 8 waves)
+    constexpr int nw_max = TM == 1 ? 16 : 8;
     int nw = 4;
     while (nw < nw_max && tiles * nw < 2048 && NG / (2 * nw) >= 4)
         nw *= 2;
     if (nw == 4)
-        return launch_cfg<SkCfg<BITS, TM, 4>>(p, stream);
-    if constexpr (TM == 1) {
+        return launch_cfg<SkCfg<BITS, TM, 4, TN>>(p, stream);
+    if constexpr (nw_max == 16) {
         if (nw == 16)
-            return launch_cfg<SkCfg<BITS, TM, 16>>(p, stream);
+            return launch_cfg<SkCfg<BITS, TM, 16, TN>>(p, stream);
     }
-    return launch_cfg<SkCfg<BITS, TM, 8>>(p, stream);
+    return launch_cfg<SkCfg<BITS, TM, 8, TN>>(p, stream);
+}
+
+template <int BITS, int TM>
+hipError_t launch_tm(const GemmProblem &p, hipStream_t stream)
+{
+    return launch_tn<BITS, TM, 2>(p, stream);
 }
 
 } // namespace
@@ -321,8 +384,9 @@ bool skinny_fits(const GemmProblem &p)
     if (p.rows < 1 || p.rows > 32)
         return false;
     const int rows_cov = p.rows <= 16 ? 16 : 32;
-    // the transposed scales must fit the 64 KB of dynamic LDS
-    return (p.k / 32) * rows_cov * 4 <= 65536;
+    // the transposed scales (whole groups of four blocks) must fit the 64 KB
+    // of dynamic LDS
+    return (p.k / 32 + 3) / 4 * 4 * rows_cov * 4 <= 65536;
 }
 
 hipError_t launch_skinny(const GemmProblem &p, hipStream_t stream)
