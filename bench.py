@@ -54,6 +54,12 @@ WORKLOADS = {
     "m16_gate": dict(m=16, k=5120, n=17408),
     "m16_down": dict(m=16, k=17408, n=5120),
     "m16_attn": dict(m=16, k=5120, n=5120),
+    # grouped expert GEMMs of the MoE workload (512 tokens, top-8 of 128
+    # experts: 4096 expert-sorted rows)
+    "moe512_gu": dict(m=4096, k=2048, n=1536, experts=128, tokens=512, src="moe512", x="x_gu",
+                      w="w_gu"),
+    "moe512_dn": dict(m=4096, k=768, n=2048, experts=128, tokens=512, src="moe512", x="x_dn",
+                      w="w_dn"),
 }
 GEMM_SRC = os.path.join(ROOT, "bit_prefill_gemm_amd", "csrc", "gemm.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_traffic.json")
@@ -74,9 +80,9 @@ def parse():
     return ap.parse_args()
 
 
-def gemm_bytes(m, k, n, bits):
+def gemm_bytes(m, k, n, bits, experts=1):
     """Algorithmic HBM bytes of one GEMM: weight image, codes, scales, fp32 output."""
-    return n * k * 18 // 32 + m * k * bits // 8 + m * (k // 32) * 4 + m * n * 4
+    return experts * n * k * 18 // 32 + m * k * bits // 8 + m * (k // 32) * 4 + m * n * 4
 
 
 def source_hash():
@@ -99,13 +105,22 @@ def measured_traffic(workload, bits):
 
 def cpu_baseline(data, wl, name, bits, seconds):
     import oracle
-    x = data["x"]
+    x = data[wl.get("x", "x")]
     m, k, n = wl["m"], wl["k"], wl["n"]
-    w, dw = oracle.q4_0_decode(data["w"], k)
+    blocks = data[wl.get("w", "w")]
+    if "experts" in wl:
+        dec = [oracle.q4_0_decode(blocks[e], k) for e in range(wl["experts"])]
+        off = data["offsets"]
+    else:
+        dec = [oracle.q4_0_decode(blocks, k)]
+        off = np.array([0, m])
     reps, t0 = 0, time.perf_counter()
     while True:
         q, d, _ = oracle.quantize(x, bits)
-        oracle.gemm_rect(q, d, w, dw, 0, m, 0, n)
+        for e, (w, dw) in enumerate(dec):
+            if off[e + 1] > off[e]:
+                oracle.gemm_rect(q[off[e]:off[e + 1]], d[off[e]:off[e + 1]], w, dw,
+                                 0, off[e + 1] - off[e], 0, n)
         reps += 1
         el = time.perf_counter() - t0
         if el >= seconds or reps >= 50:
@@ -147,11 +162,14 @@ def main():
     bb.lib()
     wl = WORKLOADS[args.workload]
     m, k, n, bits = wl["m"], wl["k"], wl["n"], args.bits
-    data = synth.make(args.workload)
-    W0 = bb.rotate_pack_weights(data["w"], bb.SRC_Q4_0_ROTATED, n, k)
+    experts = wl.get("experts", 1)
+    data = synth.make(wl.get("src", args.workload))
+    W0 = bb.rotate_pack_weights(data[wl.get("w", "w")], bb.SRC_Q4_0_ROTATED, n, k, experts)
 
     dev = torch.device("cuda:0")
-    x0 = torch.from_numpy(data["x"].view(np.int16)).to(dev).view(torch.bfloat16)
+    x0 = torch.from_numpy(data[wl.get("x", "x")].view(np.int16)).to(dev).view(torch.bfloat16)
+    offsets = (torch.from_numpy(data["offsets"].astype(np.int32)).to(dev)
+               if experts > 1 else None)
     img0 = torch.from_numpy(W0.image).to(dev)
     per_copy = img0.numel() + x0.numel() * 2
     copies = max(1, int(math.ceil(args.cold_bytes / per_copy)))
@@ -170,7 +188,10 @@ def main():
         bb.quantize_act_h32(xs[j], bits, codes=codes, scales=scales, stream=stream)
         if ev is not None:
             ev[1].record(stream)
-        bb.w4a4_gemm(codes, scales, bits, Ws[j], y=y, stream=stream)
+        if offsets is None:
+            bb.w4a4_gemm(codes, scales, bits, Ws[j], y=y, stream=stream)
+        else:
+            bb.w4a4_grouped_gemm(codes, scales, bits, offsets, Ws[j], y=y, stream=stream)
         if ev is not None:
             ev[2].record(stream)
 
@@ -193,12 +214,12 @@ def main():
     ops = 2.0 * m * n * k
     eff_tops = ops / gemm_s / 1e12
     epi_ops = 2.0 * m * n * (k // 32)     # algorithmic fp32 VALU lane-operations
-    gbytes = gemm_bytes(m, k, n, bits)
+    gbytes = gemm_bytes(m, k, n, bits, experts)
     traffic = measured_traffic(args.workload, bits)
 
     out = {
         "metric": "prompt tokens/s + effective TOPS (% int8 MFMA peak) for rotated W4A4 GEMM, M=512",
-        "value": m / (ms_per_step * 1e-3),
+        "value": wl.get("tokens", m) / (ms_per_step * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -209,13 +230,16 @@ def main():
         "vs_baseline": None,
         "dtype": "i8" if bits == 8 else "i4",
         "data": "synthetic",
-        "config": {"workload": "%s: M=%d K=%d N=%d, bf16 activations, rotated Q4_0 weights, "
-                               "%d-bit activation codes" % (args.workload, m, k, n, bits),
-                   "m": m, "k": k, "n": n, "act_bits": bits, "cold_copies": copies},
+        "config": {"workload": "%s: M=%d K=%d N=%d%s, bf16 activations, rotated Q4_0 weights, "
+                               "%d-bit activation codes"
+                               % (args.workload, m, k, n,
+                                  ", %d experts (grouped)" % experts if experts > 1 else "", bits),
+                   "m": m, "k": k, "n": n, "experts": experts, "act_bits": bits,
+                   "cold_copies": copies},
         "roofline": {"bound": "alu", "achieved": epi_ops / gemm_s / 1e12,
                      "peak": PEAK_VALU_OPS / 1e12, "unit": "T fp32 VALU lane-op/s",
                      "frac": epi_ops / gemm_s / PEAK_VALU_OPS, "traffic": traffic,
-                     "kernel": "w4a4_gemm"},
+                     "kernel": "w4a4_gemm" if experts == 1 else "w4a4_grouped_gemm"},
         "int8_mfma": {"achieved": eff_tops, "peak": PEAK_INT8_OPS / 1e12, "unit": "TOP/s",
                       "frac": eff_tops / (PEAK_INT8_OPS / 1e12)},
         "eff_TOPS": eff_tops,

@@ -88,7 +88,7 @@ struct Cfg {
     static constexpr int kPtDw = (kChDw + kThreads - 1) / kThreads;
     static constexpr int kOcc = kThreads >= 512 ? 1 : 2; // workgroups per CU aimed at
     static_assert(MF == 16 || MF == 32, "matrix tile");
-    static_assert(KC % WK == 0 && KC <= 8, "K split and swizzle range");
+    static_assert(KC % WK == 0 && KC <= 16, "K split and swizzle range");
     static_assert(KC % 4 == 0, "stages hold whole groups of four blocks");
     static_assert(kLds <= 160 * 1024, "LDS budget");
 };
@@ -131,56 +131,80 @@ __device__ __forceinline__ int xcd_remap(int w, int total)
 }
 
 // Grouped tiling: expert e owns ceil(rows_e / BM) consecutive row slots.  Find
-// the expert and the row range of `slot` with a workgroup-wide scan over the
-// clamped offsets.  Returns false (uniformly) if the slot lies beyond the last
-// tile.  Every row range returned lies inside [0, rows).
-template <int NT>
-__device__ bool grouped_slot(const int32_t *__restrict__ off, int64_t experts, int64_t rows,
-                             int bm, int slot, int *scan, int64_t &row0, int64_t &row_end,
-                             int64_t &expert)
+// the expert and the row range of `slot` with a scan over the clamped offsets
+// done by every wave on its own (no LDS, no barrier; each wave reaches the
+// same answer): lanes take four experts each, 256 experts per pass.  Returns
+// false (uniformly) if the slot lies beyond the last tile.  Every row range
+// returned lies inside [0, rows).
+template <int BM>
+__device__ bool grouped_slot(const int32_t *__restrict__ off, int64_t experts, int64_t rows64,
+                             int slot, int64_t &row0, int64_t &row_end, int64_t &expert)
 {
-    __shared__ int64_t found[4];
-    const int tid = threadIdx.x;
-    if (tid == 0)
-        found[0] = -1;
-    int64_t carry = 0;
-    for (int64_t base = 0; base < experts; base += NT) {
-        const int64_t e = base + tid;
-        int cnt = 0;
-        int64_t a = 0, b = 0;
-        if (e < experts) {
-            a = off[e];
-            b = off[e + 1];
-            a = a < 0 ? 0 : (a > rows ? rows : a);
-            b = b < 0 ? 0 : (b > rows ? rows : b);
-            if (b > a)
-                cnt = (int)((b - a + bm - 1) / bm);
+    const int lane = threadIdx.x & 63;
+    const int rows = (int)rows64; // the host limits rows to 2^31 - 1
+    int64_t carry = 0;            // slots of the experts before this pass
+    for (int64_t base = 0; base < experts; base += 256) {
+        int a[4], b[4];
+        int cnt[4], lsum = 0;
+#pragma unroll
+        for (int u = 0; u < 4; u++) {
+            const int64_t e = base + 4 * lane + u;
+            a[u] = b[u] = 0;
+            cnt[u] = 0;
+            if (e < experts) {
+                a[u] = min(max(off[e], 0), rows);
+                b[u] = min(max(off[e + 1], 0), rows);
+                if (b[u] > a[u])
+                    cnt[u] = (int)(((unsigned)(b[u] - a[u]) + BM - 1) / BM);
+            }
+            lsum += cnt[u];
         }
-        scan[tid] = cnt;
-        __syncthreads();
-        for (int d = 1; d < NT; d <<= 1) { // inclusive Hillis-Steele scan
-            const int v = tid >= d ? scan[tid - d] : 0;
-            __syncthreads();
-            scan[tid] += v;
-            __syncthreads();
+        int incl = lsum; // inclusive scan of the lanes' counts
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int v = __shfl_up(incl, d);
+            if (lane >= d)
+                incl += v;
         }
-        const int64_t incl = carry + scan[tid];
-        const int64_t excl = incl - cnt;
-        if (cnt > 0 && slot >= excl && slot < incl) {
-            found[0] = 1;
-            found[1] = a + (slot - excl) * bm;
-            found[2] = b;
-            found[3] = e;
+        const int64_t rel = slot - carry;
+        const int excl = incl - lsum;
+        const uint64_t owner = __ballot(rel >= excl && rel < incl);
+        if (owner != 0) {
+            const int src = __ffsll((unsigned long long)owner) - 1;
+            // the owning lane walks its four experts
+            int64_t r0 = 0, r1 = 0, ex = 0;
+            int64_t s = rel - excl;
+#pragma unroll
+            for (int u = 0; u < 4; u++) {
+                if (s >= 0 && s < cnt[u]) {
+                    r0 = a[u] + s * BM;
+                    r1 = b[u];
+                    ex = base + 4 * lane + u;
+                }
+                s -= cnt[u];
+            }
+            row0 = __shfl(r0, src);
+            row_end = __shfl(r1, src);
+            expert = __shfl(ex, src);
+            return true;
         }
-        carry += scan[NT - 1];
-        __syncthreads();
+        carry += __shfl(incl, 63);
     }
-    if (found[0] < 0)
-        return false;
-    row0 = found[1];
-    row_end = found[2];
-    expert = found[3];
-    return true;
+    return false;
+}
+
+// f(integral_constant<int, n>) for the runtime count 1 <= n <= N.
+template <int N, class F>
+__device__ __forceinline__ void with_count(int n, F &&f)
+{
+    if constexpr (N == 1) {
+        f(std::integral_constant<int, 1>{});
+    } else {
+        if (n >= N)
+            f(std::integral_constant<int, N>{});
+        else
+            with_count<N - 1>(n, f);
+    }
 }
 
 // Operand and result registers of the two matrix instruction shapes.
@@ -249,8 +273,7 @@ __global__ __launch_bounds__(C::kThreads, C::kOcc) void w4a4_kernel(GemmProblem 
     if (MODE == kGrouped) {
         const int slot = L / tiles_n;
         col0 = (int64_t)(L % tiles_n) * BN;
-        if (!grouped_slot<NT>(p.offsets, p.experts, p.rows, BM, slot,
-                              reinterpret_cast<int *>(lds), row0, row_end, expert))
+        if (!grouped_slot<BM>(p.offsets, p.experts, p.rows, slot, row0, row_end, expert))
             return; // uniform across the workgroup
     } else {
         row0 = (int64_t)(tm0 + L % tiles_m) * BM;
@@ -401,11 +424,19 @@ __global__ __launch_bounds__(C::kThreads, C::kOcc) void w4a4_kernel(GemmProblem 
 
     // rows of each of this wave's row tiles that hold data (uniform per wave)
     int vrows[TM];
+    int nact = 0; // row tiles with data: the first nact
 #pragma unroll
     for (int i = 0; i < TM; i++) {
         const int64_t v = row_end - (row0 + (int64_t)(wm * TM + i) * MF);
         vrows[i] = v < 0 ? 0 : (v > MF ? MF : (int)v);
+        nact += vrows[i] > 0;
     }
+    // Grouped slots often hold fewer rows than the tile (an expert's rows):
+    // the row tiles without data skip their products and epilogues.  The
+    // stage arithmetic is compiled once per count of active row tiles and
+    // chosen per stage (a uniform branch), so the tile loops stay free of
+    // branches.  The dense shapes compute every tile (padded rows are never
+    // stored).
 
     float acc[TM][TN][RG];
 #pragma unroll
@@ -471,7 +502,9 @@ __global__ __launch_bounds__(C::kThreads, C::kOcc) void w4a4_kernel(GemmProblem 
     };
 
     // One stage of arithmetic on the operands held in buffer A.
-    auto compute_stage = [&](const uint8_t *A, int kb0) {
+    auto compute_stage = [&](const uint8_t *A, int kb0, auto nact_tag) {
+        constexpr int NA = decltype(nact_tag)::value; // row tiles with data
+        auto active = [&](int i) { return i < NA; };
         const uint8_t *W = A + C::kLdsA;
         const float *Da = reinterpret_cast<const float *>(W + C::kLdsW);
         const float2 *Dw = reinterpret_cast<const float2 *>(W + C::kLdsW + C::kLdsDa);
@@ -485,7 +518,8 @@ __global__ __launch_bounds__(C::kThreads, C::kOcc) void w4a4_kernel(GemmProblem 
             Op a[TM];
 #pragma unroll
             for (int i = 0; i < TM; i++)
-                a[i] = load_a(A, kc, swz((wm * TM + i) * MF + rc, kc));
+                if (active(i))
+                    a[i] = load_a(A, kc, swz((wm * TM + i) * MF + rc, kc));
 
             if (MODE == kSums) {
 #pragma unroll
@@ -511,8 +545,9 @@ __global__ __launch_bounds__(C::kThreads, C::kOcc) void w4a4_kernel(GemmProblem 
                 for (int i = 0; i < TM; i++)
 #pragma unroll
                     for (int q = 0; q < RG / 4; q++)
-                        da[i][q] = *reinterpret_cast<const float4 *>(
-                            Da + kc * BM + (wm * TM + i) * MF + M::out_row(g, 4 * q));
+                        if (active(i))
+                            da[i][q] = *reinterpret_cast<const float4 *>(
+                                Da + kc * BM + (wm * TM + i) * MF + M::out_row(g, 4 * q));
                 // Software pipeline over the column tiles: the matrix
                 // instructions of tile j are issued before the epilogue of
                 // tile j-1, so their latency hides behind VALU work.  Padded
@@ -528,11 +563,14 @@ __global__ __launch_bounds__(C::kThreads, C::kOcc) void w4a4_kernel(GemmProblem 
                         dwc = Dw[kc * BN + (wn * TN + j) * MF + rc];
 #pragma unroll
                         for (int i = 0; i < TM; i++)
-                            Dc[i] = M::mma(a[i], b, magic);
+                            if (active(i))
+                                Dc[i] = M::mma(a[i], b, magic);
                     }
                     if (j > 0) {
 #pragma unroll
                         for (int i = 0; i < TM; i++) {
+                            if (!active(i))
+                                continue;
 #pragma unroll
                             for (int q = 0; q < RG / 4; q++) {
                                 const float dq[4] = {da[i][q].x, da[i][q].y, da[i][q].z, da[i][q].w};
@@ -579,7 +617,10 @@ __global__ __launch_bounds__(C::kThreads, C::kOcc) void w4a4_kernel(GemmProblem 
                     else
                         load_stage(kb0 + KC, std::false_type{});
                 }
-                compute_stage(lds + half * C::kStage, kb0);
+                if constexpr (MODE == kGrouped)
+                    with_count<TM>(nact, [&](auto na) { compute_stage(lds + half * C::kStage, kb0, na); });
+                else
+                    compute_stage(lds + half * C::kStage, kb0, std::integral_constant<int, TM>{});
                 if (more)
                     store_stage(lds + (half ^ 1) * C::kStage);
                 __syncthreads();
@@ -709,6 +750,7 @@ hipError_t launch_dense_bits(const GemmProblem &p, hipStream_t stream)
     }
 }
 
+// Grouped: 32-row slots; row tiles past an expert's rows are skipped.
 template <int BITS>
 hipError_t launch_grouped_bits(const GemmProblem &p, hipStream_t stream)
 {
