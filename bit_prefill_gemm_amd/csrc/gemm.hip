@@ -750,19 +750,27 @@ hipError_t launch_dense_bits(const GemmProblem &p, hipStream_t stream)
     }
 }
 
-// Grouped: 32-row slots; row tiles past an expert's rows are skipped.
+// Grouped: 32-row slots (row tiles past an expert's rows are skipped) and
+// 128 columns per workgroup: four waves of 32 x 32, each over the whole of K
+// (an expert's K is short, so splitting it across waves would leave each wave
+// too few blocks to amortise its set-up and the final reduction).
 template <int BITS>
 hipError_t launch_grouped_bits(const GemmProblem &p, hipStream_t stream)
 {
-    using C = Cfg<BITS, 16, 2, 4, 1, 1, 4, 8>;   // 32 x 64
-    using C32 = Cfg<BITS, 16, 2, 2, 1, 1, 4, 8>; // 32 x 32
+    using C128 = Cfg<BITS, 16, 2, 2, 1, 4, 1, 4>; // 32 x 128
+    using C64 = Cfg<BITS, 16, 2, 2, 1, 2, 1, 4>;  // 32 x 64
+    using C32 = Cfg<BITS, 16, 2, 2, 1, 1, 1, 4>;  // 32 x 32
     // every expert needs ceil(rows_e / BM) slots: bounded by both of these
-    int64_t slots = (p.rows + p.experts * (C::BM - 1)) / C::BM;
+    int64_t slots = (p.rows + p.experts * (C128::BM - 1)) / C128::BM;
     if (slots > p.rows)
         slots = p.rows;
-    if (p.n % C::BN == 0) {
-        const int tn = (int)(p.n / C::BN);
-        return launch_cfg<C, kGrouped>(p, 0, tn, 0, 0, slots * tn, stream);
+    if (p.n % C128::BN == 0) {
+        const int tn = (int)(p.n / C128::BN);
+        return launch_cfg<C128, kGrouped>(p, 0, tn, 0, 0, slots * tn, stream);
+    }
+    if (p.n % C64::BN == 0) {
+        const int tn = (int)(p.n / C64::BN);
+        return launch_cfg<C64, kGrouped>(p, 0, tn, 0, 0, slots * tn, stream);
     }
     const int tn = (int)(p.n / C32::BN);
     return launch_cfg<C32, kGrouped>(p, 0, tn, 0, 0, slots * tn, stream);

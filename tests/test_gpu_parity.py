@@ -310,6 +310,19 @@ def test_grouped_ragged_experts(torch):
     check_blocksums(codes, scales, 4, W, q, wq[4], [(off[4], off[5], 0, 64)], expert=4)
 
 
+@pytest.mark.parametrize("n,k,bits", [(256, 160, 4), (96, 128, 8), (128, 2080, 8), (64, 96, 4)])
+def test_grouped_ragged_shapes(torch, n, k, bits):
+    """Every grouped tile width (128, 64, 32 columns), K not a multiple of the
+    stage or of four blocks, both activation widths."""
+    rng = np.random.default_rng(n + k + bits)
+    counts = np.array([5, 0, 40, 17, 32, 64, 1])
+    E = counts.size
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    x, _ = synth.draw_activations(rng, int(off[-1]), k, "normal", 0.02, 20.0)
+    blocks = synth.draw_q4_0(rng, (E, n), k, 0.005, 0.05)
+    check_grouped(x, blocks, off, n, k, E, bits, label="ragged shapes")
+
+
 def test_grouped_leaves_rows_outside_experts(torch):
     rng = np.random.default_rng(42)
     E, n, k, rows = 2, 32, 64, 10
