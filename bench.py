@@ -10,13 +10,20 @@ the timed region; each step uses a different copy of the weights and
 activations, cycling through enough copies (>= 512 MB) that the 256 MB
 last-level cache cannot hold them.
 
+Other workloads (--workload): the long-prompt and FFN-sized GEMM, three
+weight-streaming cases with 16 tokens, and the two grouped expert GEMMs of the
+MoE workload (512 tokens routed top-8 over 128 experts; `value` counts the 512
+tokens).
+
 Prints ONE JSON line.  `value` is prompt tokens per second of the step.  The
 `roofline` object covers the GEMM kernel (the dominant kernel).  Its average
 duration is measured with HIP events recorded on the launch stream around
-every GEMM in the timed region.  The kernel is bound by its fp32 VALU
-epilogue (two VALU operations per output element and 32-block), so the
-roofline is taken against the VALU issue rate; the int8 matrix-core view
-(effective TOPS against the dense int8 peak) is reported beside it.
+every GEMM in the timed region.  With many rows the kernel is bound by its
+fp32 VALU epilogue (two VALU operations per output element and 32-block), so
+the roofline is taken against the VALU issue rate; the int8 matrix-core view
+(effective TOPS against the dense int8 peak) is reported beside it.  With 32
+rows or fewer it is bound by the weight stream: the roofline is HBM bytes per
+second against the HBM peak.
 `traffic` comes from the committed rocprofv3 counter summary for this kernel
 and workload, and is null if the kernel source changed since it was taken.
 `cpu_baseline` times the CPU oracle on the same workload (test
@@ -61,7 +68,9 @@ WORKLOADS = {
     "moe512_dn": dict(m=4096, k=768, n=2048, experts=128, tokens=512, src="moe512", x="x_dn",
                       w="w_dn"),
 }
-GEMM_SRC = os.path.join(ROOT, "bit_prefill_gemm_amd", "csrc", "gemm.hip")
+# kernel sources of the GEMM paths (the tiled and grouped kernels, and the
+# weight-stream kernel used for a few rows)
+GEMM_SRCS = [os.path.join(ROOT, "bit_prefill_gemm_amd", "csrc", f) for f in ("gemm.hip", "skinny.hip")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_traffic.json")
 
 
@@ -86,7 +95,10 @@ def gemm_bytes(m, k, n, bits, experts=1):
 
 
 def source_hash():
-    return hashlib.sha256(open(GEMM_SRC, "rb").read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for f in GEMM_SRCS:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(workload, bits):
@@ -217,6 +229,19 @@ def main():
     gbytes = gemm_bytes(m, k, n, bits, experts)
     traffic = measured_traffic(args.workload, bits)
 
+    kernel = "w4a4_gemm" if experts == 1 else "w4a4_grouped_gemm"
+    if experts == 1 and m <= 32:
+        # a few rows: the weight stream from HBM binds
+        roofline = {"bound": "hbm", "achieved": gbytes / gemm_s / 1e9, "peak": PEAK_HBM / 1e9,
+                    "unit": "GB/s", "frac": gbytes / gemm_s / PEAK_HBM, "traffic": traffic,
+                    "kernel": kernel}
+    else:
+        # the fp32 epilogue (two VALU operations per output and block) binds
+        roofline = {"bound": "alu", "achieved": epi_ops / gemm_s / 1e12,
+                    "peak": PEAK_VALU_OPS / 1e12, "unit": "T fp32 VALU lane-op/s",
+                    "frac": epi_ops / gemm_s / PEAK_VALU_OPS, "traffic": traffic,
+                    "kernel": kernel}
+
     out = {
         "metric": "prompt tokens/s + effective TOPS (% int8 MFMA peak) for rotated W4A4 GEMM, M=512",
         "value": wl.get("tokens", m) / (ms_per_step * 1e-3),
@@ -236,10 +261,7 @@ def main():
                                   ", %d experts (grouped)" % experts if experts > 1 else "", bits),
                    "m": m, "k": k, "n": n, "experts": experts, "act_bits": bits,
                    "cold_copies": copies},
-        "roofline": {"bound": "alu", "achieved": epi_ops / gemm_s / 1e12,
-                     "peak": PEAK_VALU_OPS / 1e12, "unit": "T fp32 VALU lane-op/s",
-                     "frac": epi_ops / gemm_s / PEAK_VALU_OPS, "traffic": traffic,
-                     "kernel": "w4a4_gemm" if experts == 1 else "w4a4_grouped_gemm"},
+        "roofline": roofline,
         "int8_mfma": {"achieved": eff_tops, "peak": PEAK_INT8_OPS / 1e12, "unit": "TOP/s",
                       "frac": eff_tops / (PEAK_INT8_OPS / 1e12)},
         "eff_TOPS": eff_tops,
