@@ -692,9 +692,8 @@ hipError_t launch_dense_cfg(const GemmProblem &p, hipStream_t stream)
 // workgroups on one CU finish at different times: the older one gets issue
 // priority and the younger then runs alone).  KC = 8 blocks per stage.
 template <int BITS> struct Tiles {
-    // 64 x 160: two column halves of 64 x 80 (16x16 tiles), K split in four
-    // (8-bit codes stage 4 blocks at a time to stay within 256 registers)
-    using W64x160 = Cfg<BITS, 16, 4, 5, 1, 2, 4, BITS == 8 ? 4 : 8>;
+    // 64 x 160: two row halves of 32 x 160 (32x32 tiles), K split in four
+    using W64x160 = Cfg<BITS, 32, 1, 5, 2, 1, 4, 8>;
     // 64 x 128: two row halves of 32 x 128, K split in four
     using W64x128 = Cfg<BITS, 32, 1, 4, 2, 1, 4, 8>;
     // 64 x 64 and 64 x 32: four waves of 16x16 tiles, K split in four (two

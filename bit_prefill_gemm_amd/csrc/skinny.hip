@@ -41,16 +41,16 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 constexpr int kMagicBits = 0x4B400000;
 constexpr float kMagic = 12582912.0f;
 
-template <int BITS_, int TM_, int NW_, int TN_>
+template <int BITS_, int TM_, int NW_, int TN_, int D_>
 struct SkCfg {
     static constexpr int BITS = BITS_, TM = TM_, NW = NW_;
     static constexpr int TN = TN_;                    // 16-column tiles per workgroup (2: one image tile)
     static constexpr int kCols = 16 * TN;
-    // groups of four blocks in flight per wave: one.  Deeper rings measured
-    // slower: with every wave of the grid streaming, more outstanding reads
-    // only lengthen the memory queues (the waves of a SIMD still overlap one
-    // another's waits).
-    static constexpr int D = 1;
+    // groups of four blocks in flight per wave: one when a wave walks many
+    // groups, two when it walks few.  Deeper rings measured slower: with every
+    // wave of the grid streaming, more outstanding reads only lengthen the
+    // memory queues (the waves of a SIMD still overlap one another's waits).
+    static constexpr int D = D_;
     static constexpr int kThreads = 64 * NW;
     static constexpr int kRows = 16 * TM;             // rows covered (M <= kRows)
     static constexpr int kAB = BITS == 4 ? 16 : 32;   // code bytes per (row, block)
@@ -251,28 +251,22 @@ __global__ __launch_bounds__(C::kThreads) void skinny_kernel(GemmProblem p)
     // keeps the order of outstanding loads the same in every iteration; the
     // scheduling barriers keep the prologue's loads in that same slot order.
     // Activation scales, transposed to [block][row]; zero past M and for the
-    // blocks of the last group past B.  The first kDaU per thread are loaded
-    // before the operand prologue and stored behind it, so both latencies
-    // overlap.
-    constexpr int kDaU = NW >= 16 ? 8 : 16;
-    const int da_total = 4 * NG * kRows;
-    float dv[kDaU];
-    auto da_load = [&](int base) {
+    // blocks of the last group past B.  A thread takes block columns b = tid,
+    // tid + NT, ... and all kRows rows of each (coalesced reads along b, no
+    // index division).  The first column's loads are issued before the
+    // operand prologue and stored behind it, so both latencies overlap.
+    const int da_cols = 4 * NG;
+    float dv[kRows];
+    auto da_load = [&](int b) {
 #pragma unroll
-        for (int u = 0; u < kDaU; u++) {
-            const int idx = base + u * NT;
-            const int m = idx / (4 * NG), b = idx - m * (4 * NG);
-            dv[u] = idx < da_total && m < rows && b < B ? p.scales[(int64_t)m * B + b] : 0.0f;
-        }
+        for (int m = 0; m < kRows; m++)
+            dv[m] = b < B && m < rows ? p.scales[(int64_t)m * B + b] : 0.0f;
     };
-    auto da_store = [&](int base) {
+    auto da_store = [&](int b) {
+        if (b < da_cols)
 #pragma unroll
-        for (int u = 0; u < kDaU; u++) {
-            const int idx = base + u * NT;
-            const int m = idx / (4 * NG), b = idx - m * (4 * NG);
-            if (idx < da_total)
-                Da[b * kRows + m] = dv[u];
-        }
+            for (int m = 0; m < kRows; m++)
+                Da[b * kRows + m] = dv[m];
     };
     da_load(tid);
     __builtin_amdgcn_sched_barrier(0);
@@ -295,9 +289,9 @@ __global__ __launch_bounds__(C::kThreads) void skinny_kernel(GemmProblem p)
     }
 
     da_store(tid);
-    for (int base = tid + kDaU * NT; base < da_total; base += kDaU * NT) {
-        da_load(base);
-        da_store(base);
+    for (int b = tid + NT; b < da_cols; b += NT) {
+        da_load(b);
+        da_store(b);
     }
     __syncthreads(); // the scales in LDS
 
@@ -353,6 +347,20 @@ hipError_t launch_cfg(const GemmProblem &p, hipStream_t stream)
 
 // Waves per workgroup: enough waves in the whole grid to keep the weight
 // stream busy (about 8 per CU), each with at least 4 groups of K.
+template <int BITS, int TM, int TN, int D>
+hipError_t launch_nw(const GemmProblem &p, int nw, hipStream_t stream)
+{
+    if (nw == 4)
+        return launch_cfg<SkCfg<BITS, TM, 4, TN, D>>(p, stream);
+    if constexpr (TM == 1) {
+        if (nw == 16)
+            return launch_cfg<SkCfg<BITS, TM, 16, TN, D>>(p, stream);
+    }
+    return launch_cfg<SkCfg<BITS, TM, 8, TN, D>>(p, stream);
+}
+
+// Waves per workgroup: enough waves in the whole grid to keep the weight
+// stream busy (about 8 per CU), each with at least 4 groups of K.
 template <int BITS, int TM, int TN>
 hipError_t launch_tn(const GemmProblem &p, hipStream_t stream)
 {
@@ -362,13 +370,9 @@ hipError_t launch_tn(const GemmProblem &p, hipStream_t stream)
     int nw = 4;
     while (nw < nw_max && tiles * nw < 2048 && NG / (2 * nw) >= 4)
         nw *= 2;
-    if (nw == 4)
-        return launch_cfg<SkCfg<BITS, TM, 4, TN>>(p, stream);
-    if constexpr (nw_max == 16) {
-        if (nw == 16)
-            return launch_cfg<SkCfg<BITS, TM, 16, TN>>(p, stream);
-    }
-    return launch_cfg<SkCfg<BITS, TM, 8, TN>>(p, stream);
+    if (NG / nw <= 6)
+        return launch_nw<BITS, TM, TN, 2>(p, nw, stream);
+    return launch_nw<BITS, TM, TN, 1>(p, nw, stream);
 }
 
 template <int BITS, int TM>
