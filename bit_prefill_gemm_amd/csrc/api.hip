@@ -52,9 +52,13 @@ uint64_t image_bytes(int64_t n, int64_t k, int64_t e)
     return (uint64_t)e * (uint64_t)(n / 32) * (uint64_t)block_groups(k) * 2304u;
 }
 
+// the scales of a group sit after its 2048 code bytes, inside its 2304-byte block
 uint64_t scales_offset(int64_t n, int64_t k, int64_t e)
 {
-    return (uint64_t)e * (uint64_t)(n / 32) * (uint64_t)block_groups(k) * 2048u;
+    (void)n;
+    (void)k;
+    (void)e;
+    return 2048u;
 }
 
 bool shape_ok(int64_t n, int64_t k, int64_t e)
@@ -74,7 +78,7 @@ bool shape_ok(int64_t n, int64_t k, int64_t e)
 bpg_status check_stamp(const bpg_weights_desc *w)
 {
     if (w->magic != BPG_WEIGHTS_MAGIC || w->version != BPG_WEIGHTS_VERSION ||
-        w->rotation != 32 || w->layout != BPG_LAYOUT_COLTILE32_K4)
+        w->rotation != 32 || w->layout != BPG_LAYOUT_GROUP4)
         return BPG_ERR_STAMP;
     if (!shape_ok(w->n, w->k, w->num_experts))
         return BPG_ERR_STAMP;
@@ -162,16 +166,17 @@ void quantize_weight_block(const double in[32], uint8_t blk[18])
 }
 
 // Place one canonical 18-byte block of (expert e, row n, block b) in the
-// image: its four code dwords go to slots s = 0..3 of (tile, group), the
-// scale next to the scales of the group's other blocks.
+// image: its four code dwords go to slots s = 0..3 of its (tile, group)
+// block, its scale to the group's scale area (column c = 16h + c16 at
+// [c16][h][q]).
 inline void place_block(const uint8_t blk[18], int64_t e, int64_t n, int64_t b, int64_t N,
-                        int64_t G, uint8_t *codes, uint16_t *scales)
+                        int64_t G, uint8_t *img)
 {
-    const int64_t tg = (e * (N / 32) + n / 32) * G + b / 4; // (expert, column tile, group)
+    uint8_t *grp = img + ((e * (N / 32) + n / 32) * G + b / 4) * 2304;
     const int64_t c = n % 32, q = b % 4;
     for (int s = 0; s < 4; s++)
-        std::memcpy(codes + tg * 2048 + ((s * 32 + c) * 4 + q) * 4, blk + 2 + 4 * s, 4);
-    scales[tg * 128 + c * 4 + q] = (uint16_t)(blk[0] | (blk[1] << 8));
+        std::memcpy(grp + ((s * 32 + c) * 4 + q) * 4, blk + 2 + 4 * s, 4);
+    std::memcpy(grp + 2048 + (((c % 16) * 2 + c / 16) * 4 + q) * 2, blk, 2);
 }
 
 } // namespace
@@ -216,12 +221,12 @@ bpg_status rotate_pack_weights(const void *src, bpg_src_kind kind, int64_t n, in
         return BPG_ERR_BUFFER;
 
     const int64_t B = k / 32, G = block_groups(k);
-    uint8_t *codes = static_cast<uint8_t *>(dst_host);
-    const uint64_t soff = scales_offset(n, k, num_experts);
-    uint16_t *scales = reinterpret_cast<uint16_t *>(codes + soff);
+    uint8_t *img = static_cast<uint8_t *>(dst_host);
     // blocks past B: codes 0x88 (value 0), scale 0
-    std::memset(codes, 0x88, soff);
-    std::memset(codes + soff, 0, total - soff);
+    for (uint64_t off = 0; off < total; off += 2304) {
+        std::memset(img + off, 0x88, 2048);
+        std::memset(img + off + 2048, 0, 256);
+    }
     for (int64_t e = 0; e < num_experts; e++)
         for (int64_t r = 0; r < n; r++)
             for (int64_t b = 0; b < B; b++) {
@@ -244,7 +249,7 @@ bpg_status rotate_pack_weights(const void *src, bpg_src_kind kind, int64_t n, in
                     }
                     quantize_weight_block(in, blk);
                 }
-                place_block(blk, e, r, b, n, G, codes, scales);
+                place_block(blk, e, r, b, n, G, img);
             }
 
     bpg_weights_desc d;
@@ -252,7 +257,7 @@ bpg_status rotate_pack_weights(const void *src, bpg_src_kind kind, int64_t n, in
     d.magic = BPG_WEIGHTS_MAGIC;
     d.version = BPG_WEIGHTS_VERSION;
     d.rotation = 32;
-    d.layout = BPG_LAYOUT_COLTILE32_K4;
+    d.layout = BPG_LAYOUT_GROUP4;
     d.n = n;
     d.k = k;
     d.num_experts = num_experts;

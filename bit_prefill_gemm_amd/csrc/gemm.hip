@@ -291,9 +291,12 @@ __global__ __launch_bounds__(C::kThreads, C::kOcc) void w4a4_kernel(GemmProblem 
     //      output rows that are never stored.
     // (every offset below stays under 2^31 for K <= 2^22)
     const uint8_t *__restrict__ a_base0 = p.codes + row0 * arow_bytes;
-    const uint8_t *__restrict__ w_base0 = p.wcodes + (expert * ntiles32 + ct0) * NG * 2048;
+    // weight image: 2304-byte blocks per (expert, 32-column tile, group of
+    // four K-blocks): 2048 code bytes, then 128 fp16 scales (p.wscales points
+    // at the first block's scales)
+    const uint8_t *__restrict__ w_base0 = p.wcodes + (expert * ntiles32 + ct0) * NG * 2304;
     const float *__restrict__ da_base0 = p.scales + row0 * B;
-    const uint16_t *__restrict__ dw_base0 = p.wscales + (expert * ntiles32 + ct0) * NG * 128;
+    const uint16_t *__restrict__ dw_base0 = p.wscales + (expert * ntiles32 + ct0) * NG * 1152;
     const int last_row = (int)(row_end - 1 - row0); // >= 0
 
     uint32_t oa[C::kPtA], la[C::kPtA], ow[C::kPtW], lw[C::kPtW];
@@ -322,7 +325,7 @@ __global__ __launch_bounds__(C::kThreads, C::kOcc) void w4a4_kernel(GemmProblem 
         const int cc = c < C::kChW ? c : 0;
         const int s = cc & 3, col = (cc >> 2) % BN, gs = (cc >> 2) / BN;
         const int64_t gcol = col0 + col;
-        ow[i] = (uint32_t)((((gcol >> 5) - ct0) * NG + gs) * 2048 + (s * 32 + (gcol & 31)) * 16);
+        ow[i] = (uint32_t)((((gcol >> 5) - ct0) * NG + gs) * 2304 + (s * 32 + (gcol & 31)) * 16);
         lw[i] = (uint32_t)((4 * gs * BN + col) * 16 + 4 * s); // block 4*gs; + q*BN*16 for 4*gs+q
         kcw[i] = (int8_t)(c < C::kChW ? 4 * gs : 127);
     }
@@ -343,7 +346,8 @@ __global__ __launch_bounds__(C::kThreads, C::kOcc) void w4a4_kernel(GemmProblem 
         const int cc = c < C::kChDw ? c : 0;
         const int gs = cc / BN, col = cc % BN;
         const int64_t gcol = col0 + col;
-        odw[i] = (uint32_t)((((gcol >> 5) - ct0) * NG + gs) * 128 + (gcol & 31) * 4);
+        const int c32 = (int)(gcol & 31);
+        odw[i] = (uint32_t)((((gcol >> 5) - ct0) * NG + gs) * 1152 + ((c32 % 16) * 2 + c32 / 16) * 4);
         ldw_[i] = (uint32_t)(4 * gs * BN + col);
         kcdw[i] = (int8_t)(c < C::kChDw ? 4 * gs : 127);
     }
@@ -364,9 +368,9 @@ __global__ __launch_bounds__(C::kThreads, C::kOcc) void w4a4_kernel(GemmProblem 
         constexpr bool full = decltype(full_tag)::value;
         const int kv = full ? KC : B - kb0;
         const uint8_t *ab = a_base0 + kb0 * kAB;
-        const uint8_t *wb = w_base0 + kb0 * 512;
+        const uint8_t *wb = w_base0 + kb0 * 576;   // kb0 / 4 groups of 2304 bytes
         const float *dab = da_base0 + kb0;
-        const uint16_t *dwb = dw_base0 + kb0 * 32; // kb0 / 4 groups of 128 scales
+        const uint16_t *dwb = dw_base0 + kb0 * 288; // kb0 / 4 groups, 1152 fp16 apart
 #pragma unroll
         for (int i = 0; i < C::kPtA; i++)
             ra[i] = (full || kca[i] < kv)

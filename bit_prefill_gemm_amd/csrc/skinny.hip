@@ -44,7 +44,8 @@ constexpr float kMagic = 12582912.0f;
 template <int BITS_, int TM_, int NW_, int TN_, int D_>
 struct SkCfg {
     static constexpr int BITS = BITS_, TM = TM_, NW = NW_;
-    static constexpr int TN = TN_;                    // 16-column tiles per workgroup (2: one image tile)
+    static constexpr int TN = TN_;                    // 16-column tiles per workgroup: one image tile
+    static_assert(TN == 2, "one 32-column image tile per workgroup");
     static constexpr int kCols = 16 * TN;
     // groups of four blocks in flight per wave: one when a wave walks many
     // groups, two when it walks few.  Deeper rings measured slower: with every
@@ -81,19 +82,12 @@ __device__ __forceinline__ gptr uniform_ptr(const void *p)
     return (gptr)(((uint64_t)hi << 32) | lo);
 }
 
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ uint4 gload16(gptr base, uint32_t off)
 {
     const u32x4 v = *(const __attribute__((address_space(1))) u32x4 *)(base + off);
     return make_uint4(v.x, v.y, v.z, v.w);
-}
-
-__device__ __forceinline__ uint2 gload8(gptr base, uint32_t off)
-{
-    const u32x2 v = *(const __attribute__((address_space(1))) u32x2 *)(base + off);
-    return make_uint2(v.x, v.y);
 }
 
 // 4x4 transpose across the four 16-lane rows of a wave: on entry register q
@@ -139,9 +133,11 @@ __global__ __launch_bounds__(C::kThreads) void skinny_kernel(GemmProblem p)
     const int g1 = (int)((int64_t)(wave + 1) * NG / NW);
     const int64_t arow = p.k * kAB / 32;
     const gptr a_base = uniform_ptr(p.codes);
-    const gptr w_base = uniform_ptr(p.wcodes + (col0 / 32) * NG * 2048);
-    const gptr dw_base = uniform_ptr(p.wscales + (col0 / 32) * NG * 128);
-    uint32_t va[TM], vw[TN], vdw[TN];
+    const gptr w_base = uniform_ptr(p.wcodes + (col0 / 32) * NG * 2304);
+    uint32_t va[TM], vw[TN];
+    // the group's scales: 16 bytes at [c16 = c] = column c's and column
+    // 16 + c's four blocks
+    const uint32_t vdw = (uint32_t)(2048 + c * 16);
 #pragma unroll
     for (int i = 0; i < TM; i++) {
         const int m = 16 * i + c;
@@ -149,23 +145,20 @@ __global__ __launch_bounds__(C::kThreads) void skinny_kernel(GemmProblem p)
     }
 #pragma unroll
     for (int j = 0; j < TN; j++) {
-        // 16-column tile j is half j % 2 of image tile j / 2
-        vw[j] = (uint32_t)((j / 2) * NG * 2048 + (g * 32 + 16 * (j % 2) + c) * 16);
-        vdw[j] = (uint32_t)((j / 2) * NG * 256 + (16 * (j % 2) + c) * 8);
+        // 16-column tile j is half j of the image tile
+        vw[j] = (uint32_t)((g * 32 + 16 * j + c) * 16);
     }
 
     // ring of D groups of operands in registers
-    uint4 rw[D][TN], ra[D][TM][kAH];
-    uint2 rdw[D][TN];
+    uint4 rw[D][TN], ra[D][TM][kAH], rdw[D];
     auto load = [&](int d, int G) {
-        const gptr wb = w_base + G * 2048, dwb = dw_base + G * 256;
+        const gptr wb = w_base + G * 2304;
         // the last group may end past block B-1: those lanes re-read block B-1
         const int bq = min(4 * G + g, B - 1);
 #pragma unroll
-        for (int j = 0; j < TN; j++) {
+        for (int j = 0; j < TN; j++)
             rw[d][j] = gload16(wb, vw[j]);
-            rdw[d][j] = gload8(dwb, vdw[j]);
-        }
+        rdw[d] = gload16(wb, vdw);
 #pragma unroll
         for (int i = 0; i < TM; i++)
 #pragma unroll
@@ -228,7 +221,7 @@ __global__ __launch_bounds__(C::kThreads) void skinny_kernel(GemmProblem p)
                 da[i] = *reinterpret_cast<const float4 *>(Da + b * kRows + 16 * i + 4 * g);
 #pragma unroll
             for (int j = 0; j < TN; j++) {
-                const uint32_t hp = q < 2 ? rdw[d][j].x : rdw[d][j].y;
+                const uint32_t hp = j == 0 ? (q < 2 ? rdw[d].x : rdw[d].y) : (q < 2 ? rdw[d].z : rdw[d].w);
                 const uint16_t hb = (uint16_t)((q & 1) ? hp >> 16 : hp & 0xFFFFu);
                 const float dw = (float)__builtin_bit_cast(_Float16, hb);
                 const float cm = -kMagic * dw; // exact: dw has 11 significant bits

@@ -79,36 +79,39 @@ typedef enum { BPG_X_F32 = 0, BPG_X_BF16 = 1 } bpg_x_dtype;
 
 #define BPG_WEIGHTS_MAGIC 0x57475042u /* "BPGW" little-endian */
 #define BPG_WEIGHTS_VERSION 1u
-#define BPG_LAYOUT_COLTILE32_K4 2u
+#define BPG_LAYOUT_GROUP4 3u
 
 /*
  * Stamp of a packed weight image (the analogue of the rotated file's stamp:
  * a GEMM refuses an image whose stamp is missing or does not say rotated).
  *
- * Device image, layout BPG_LAYOUT_COLTILE32_K4, for E experts (1 if dense),
+ * Device image, layout BPG_LAYOUT_GROUP4, for E experts (1 if dense),
  * B = K/32 blocks per row, G = ceil(B/4) groups of four blocks and T = N/32
- * column tiles of 32 columns:
- *   codes  at byte 0:           uint32 [E][T][G][4 slots s][32 columns][4 blocks q]:
- *          dword s (bytes 4s..4s+3) of the 16 Q4_0 nibble bytes of column
- *          32t+c, block 4G+q (byte j: element j in the low nibble, element
- *          j+16 in the high nibble; code u means u-8);
- *   scales at scales_offset:    fp16 [E][T][G][32 columns][4 blocks q], the
- *          block scale.
+ * column tiles of 32 columns: one 2304-byte block per (expert, tile, group),
+ * in that order ([E][T][G]), holding
+ *   bytes 0..2047:     uint32 [4 slots s][32 columns c][4 blocks q]: dword s
+ *                      (bytes 4s..4s+3) of the 16 Q4_0 nibble bytes of column
+ *                      32t+c, block 4G+q (byte j: element j in the low nibble,
+ *                      element j+16 in the high nibble; code u means u-8);
+ *   bytes 2048..2303:  fp16 [16][2][4 blocks q]: the block scale of column
+ *                      c = 16h + c16 at [c16][h][q].
  * Blocks past B (when B is not a multiple of 4) hold codes 0x88 (value 0)
- * and scale 0.  One 16-byte read at (t, G, s, c) holds slot s of column c for
- * four consecutive blocks.  Total bytes = E*T*G*2304 (= E*N*K*18/32, as for
- * Q4_0, when K is a multiple of 128).
+ * and scale 0.  One 16-byte read at (s, c) holds slot s of column c for four
+ * consecutive blocks; one at scale row c16 holds the four scales of columns
+ * c16 and 16 + c16.  Total bytes = E*T*G*2304 (= E*N*K*18/32, as for Q4_0,
+ * when K is a multiple of 128).  scales_offset is 2048: the offset of a
+ * group's scales inside its block.
  */
 typedef struct {
     uint32_t magic;        /* BPG_WEIGHTS_MAGIC */
     uint32_t version;      /* BPG_WEIGHTS_VERSION */
     uint32_t rotation;     /* 32: every block rotated by H32 */
-    uint32_t layout;       /* BPG_LAYOUT_COLTILE32_K4 */
+    uint32_t layout;       /* BPG_LAYOUT_GROUP4 */
     int64_t n;             /* output channels per expert */
     int64_t k;             /* input channels */
     int64_t num_experts;   /* 1 for a dense weight */
     uint64_t bytes;        /* size of the image */
-    uint64_t scales_offset;/* byte offset of the scales region */
+    uint64_t scales_offset;/* 2048: offset of a group's scales in its block */
 } bpg_weights_desc;
 
 /* Human-readable name of a status (static string). */

@@ -47,11 +47,11 @@ def test_status_strings():
 
 def good_desc(n=64, k=128, e=1):
     d = bb.WeightsDesc()
-    d.magic, d.version, d.rotation, d.layout = 0x57475042, 1, 32, 2
+    d.magic, d.version, d.rotation, d.layout = 0x57475042, 1, 32, 3
     d.n, d.k, d.num_experts = n, k, e
     groups = (k // 32 + 3) // 4
     d.bytes = e * (n // 32) * groups * 2304
-    d.scales_offset = e * (n // 32) * groups * 2048
+    d.scales_offset = 2048
     return d
 
 
@@ -102,7 +102,8 @@ def _desc_with(**kw):
     (dict(desc=_desc_with(rotation=0)), STAMP),      # an unrotated image is refused
     (dict(desc=_desc_with(rotation=64)), STAMP),
     (dict(desc=_desc_with(layout=0)), STAMP),
-    (dict(desc=_desc_with(layout=1)), STAMP),        # the earlier, non-interleaved layout
+    (dict(desc=_desc_with(layout=1)), STAMP),        # earlier layouts
+    (dict(desc=_desc_with(layout=2)), STAMP),
     (dict(desc=_desc_with(bytes=1)), STAMP),
     (dict(desc=_desc_with(scales_offset=8)), STAMP),
     (dict(desc=_desc_with(n=48)), STAMP),

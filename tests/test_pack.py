@@ -9,13 +9,17 @@ from bit_prefill_gemm_amd import synth
 
 
 def image_regions(img: np.ndarray, n: int, k: int, e: int):
-    """The documented regions: codes uint32 [e][n/32][G][4 slots][32 cols][4 blocks],
-    scales fp16 bits [e][n/32][G][32 cols][4 blocks], G = ceil(k/128)."""
+    """The documented layout: one 2304-byte block per (expert, tile, group of four
+    blocks): codes uint32 [4 slots][32 cols][4 blocks], then scales fp16 bits
+    [16][2][4 blocks] (column 16h + c16 at [c16][h]).  Returns codes
+    [e][n/32][G][4][32][4] and scales [e][n/32][G][32 cols][4 blocks]."""
     B = k // 32
     G, T = (B + 3) // 4, n // 32
     assert img.size == e * T * G * 2304
-    codes = img[: e * T * G * 2048].view("<u4").reshape(e, T, G, 4, 32, 4)
-    scales = img[e * T * G * 2048:].view("<u2").reshape(e, T, G, 32, 4)
+    blk = img.reshape(e, T, G, 2304)
+    codes = np.ascontiguousarray(blk[..., :2048]).view("<u4").reshape(e, T, G, 4, 32, 4)
+    sc = np.ascontiguousarray(blk[..., 2048:]).view("<u2").reshape(e, T, G, 16, 2, 4)
+    scales = sc.transpose(0, 1, 2, 4, 3, 5).reshape(e, T, G, 32, 4)   # [h][c16] -> column
     return codes, scales
 
 
