@@ -8,7 +8,8 @@ against Q4_0 weights that were rotated the same way offline.
 Public names mirror the C ABI in include/bpg.h:
 
     rotate_pack_weights, quantize_act_h32, w4a4_gemm, w4a4_grouped_gemm,
-    w4a4_gemm_blocksums
+    w4a4_gemm_blocksums, and the unrotated route's pack_weights_unrotated,
+    quantize_act_unrotated, w4a4_gemm_unrotated
 
 The binding is loaded lazily so that ``bit_prefill_gemm_amd.synth`` (input
 generators) imports without the HIP library.
@@ -16,7 +17,8 @@ generators) imports without the HIP library.
 _BINDING_NAMES = {
     "rotate_pack_weights", "rotate_pack_weights_bytes", "quantize_act_h32", "w4a4_gemm",
     "w4a4_grouped_gemm", "w4a4_gemm_blocksums", "Weights", "WeightsDesc", "BpgError",
-    "SRC_F32", "SRC_BF16", "SRC_Q4_0_ROTATED", "X_F32", "X_BF16",
+    "SRC_F32", "SRC_BF16", "SRC_Q4_0_ROTATED", "SRC_Q4_0", "X_F32", "X_BF16",
+    "pack_weights_unrotated", "quantize_act_unrotated", "w4a4_gemm_unrotated",
 }
 
 

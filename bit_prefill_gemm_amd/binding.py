@@ -20,11 +20,12 @@ STATUS_NAMES = {0: "BPG_OK", 1: "BPG_ERR_NULL", 2: "BPG_ERR_SHAPE", 3: "BPG_ERR_
                 4: "BPG_ERR_DTYPE", 5: "BPG_ERR_STAMP", 6: "BPG_ERR_BUFFER",
                 7: "BPG_ERR_DEVICE", 8: "BPG_ERR_LAUNCH"}
 
-SRC_F32, SRC_BF16, SRC_Q4_0_ROTATED = 0, 1, 2
+SRC_F32, SRC_BF16, SRC_Q4_0_ROTATED, SRC_Q4_0 = 0, 1, 2, 3
 X_F32, X_BF16 = 0, 1
 
 ENTRY_POINTS = ("bpg_status_str", "rotate_pack_weights_bytes", "rotate_pack_weights",
-                "quantize_act_h32", "w4a4_gemm", "w4a4_grouped_gemm", "w4a4_gemm_blocksums")
+                "quantize_act_h32", "w4a4_gemm", "w4a4_grouped_gemm", "w4a4_gemm_blocksums",
+                "pack_weights_unrotated", "quantize_act_unrotated", "w4a4_gemm_unrotated")
 
 
 class WeightsDesc(ctypes.Structure):
@@ -58,15 +59,20 @@ def _lib_handle():
     lib.bpg_status_str.argtypes = [ctypes.c_int]
     lib.rotate_pack_weights_bytes.restype = ctypes.c_size_t
     lib.rotate_pack_weights_bytes.argtypes = [_i64, _i64, _i64]
-    lib.rotate_pack_weights.restype = ctypes.c_int
-    lib.rotate_pack_weights.argtypes = [_vp, ctypes.c_int, _i64, _i64, _i64, _vp, ctypes.c_size_t,
-                                        ctypes.POINTER(WeightsDesc)]
-    lib.quantize_act_h32.restype = ctypes.c_int
-    lib.quantize_act_h32.argtypes = [_vp, ctypes.c_int, _i64, _i64, _i64, ctypes.c_int, _vp, _vp,
-                                     _vp]
-    lib.w4a4_gemm.restype = ctypes.c_int
-    lib.w4a4_gemm.argtypes = [_vp, _vp, ctypes.c_int, _i64, ctypes.POINTER(WeightsDesc), _vp, _vp,
-                              _i64, _vp]
+    for name in ("rotate_pack_weights", "pack_weights_unrotated"):
+        fn = getattr(lib, name)
+        fn.restype = ctypes.c_int
+        fn.argtypes = [_vp, ctypes.c_int, _i64, _i64, _i64, _vp, ctypes.c_size_t,
+                       ctypes.POINTER(WeightsDesc)]
+    for name in ("quantize_act_h32", "quantize_act_unrotated"):
+        fn = getattr(lib, name)
+        fn.restype = ctypes.c_int
+        fn.argtypes = [_vp, ctypes.c_int, _i64, _i64, _i64, ctypes.c_int, _vp, _vp, _vp]
+    for name in ("w4a4_gemm", "w4a4_gemm_unrotated"):
+        fn = getattr(lib, name)
+        fn.restype = ctypes.c_int
+        fn.argtypes = [_vp, _vp, ctypes.c_int, _i64, ctypes.POINTER(WeightsDesc), _vp, _vp,
+                       _i64, _vp]
     lib.w4a4_grouped_gemm.restype = ctypes.c_int
     lib.w4a4_grouped_gemm.argtypes = [_vp, _vp, ctypes.c_int, _i64, _vp,
                                       ctypes.POINTER(WeightsDesc), _vp, _vp, _i64, _vp]
@@ -139,24 +145,32 @@ def rotate_pack_weights_bytes(n: int, k: int, num_experts: int = 1) -> int:
     return int(_lib_handle().rotate_pack_weights_bytes(n, k, num_experts))
 
 
-def rotate_pack_weights(src: np.ndarray, kind: int, n: int, k: int,
-                        num_experts: int = 1) -> Weights:
-    """Host-side packing; returns Weights with a numpy image (call .to(device))."""
+def _pack(name: str, src: np.ndarray, kind: int, n: int, k: int, num_experts: int) -> Weights:
     src = np.ascontiguousarray(src)
     nbytes = rotate_pack_weights_bytes(n, k, num_experts)
     if nbytes == 0:
-        raise BpgError(2, "rotate_pack_weights")
+        raise BpgError(2, name)
     img = np.empty(nbytes, dtype=np.uint8)
     desc = WeightsDesc()
-    st = _lib_handle().rotate_pack_weights(src.ctypes.data_as(_vp), kind, n, k, num_experts,
-                                           img.ctypes.data_as(_vp), img.nbytes,
-                                           ctypes.byref(desc))
-    _check(st, "rotate_pack_weights")
+    st = getattr(_lib_handle(), name)(src.ctypes.data_as(_vp), kind, n, k, num_experts,
+                                      img.ctypes.data_as(_vp), img.nbytes, ctypes.byref(desc))
+    _check(st, name)
     return Weights(desc, img)
 
 
-def quantize_act_h32(x, act_bits: int = 4, codes=None, scales=None, stream=None):
-    """x: 2-D cuda tensor (float32 or bfloat16, unit stride along K).  Returns (codes, scales)."""
+def rotate_pack_weights(src: np.ndarray, kind: int, n: int, k: int,
+                        num_experts: int = 1) -> Weights:
+    """Host-side packing; returns Weights with a numpy image (call .to(device))."""
+    return _pack("rotate_pack_weights", src, kind, n, k, num_experts)
+
+
+def pack_weights_unrotated(src: np.ndarray, kind: int, n: int, k: int,
+                           num_experts: int = 1) -> Weights:
+    """Host-side packing of the unrotated route (stamp rotation 0)."""
+    return _pack("pack_weights_unrotated", src, kind, n, k, num_experts)
+
+
+def _quantize(name: str, x, act_bits, codes, scales, stream):
     torch = _torch()
     if x.dim() != 2 or x.stride(1) != 1:
         raise ValueError("x must be a 2-D tensor with unit stride along K")
@@ -169,22 +183,41 @@ def quantize_act_h32(x, act_bits: int = 4, codes=None, scales=None, stream=None)
                             device=x.device)
     if scales is None:
         scales = torch.empty((m, k // 32), dtype=torch.float32, device=x.device)
-    st = _lib_handle().quantize_act_h32(_dptr(x), dt, m, k, x.stride(0), act_bits, _dptr(codes),
-                                        _dptr(scales), _stream_handle(stream))
-    _check(st, "quantize_act_h32")
+    st = getattr(_lib_handle(), name)(_dptr(x), dt, m, k, x.stride(0), act_bits, _dptr(codes),
+                                      _dptr(scales), _stream_handle(stream))
+    _check(st, name)
     return codes, scales
 
 
-def w4a4_gemm(codes, scales, act_bits: int, w: Weights, y=None, stream=None):
+def quantize_act_h32(x, act_bits: int = 4, codes=None, scales=None, stream=None):
+    """x: 2-D cuda tensor (float32 or bfloat16, unit stride along K).  Returns (codes, scales)."""
+    return _quantize("quantize_act_h32", x, act_bits, codes, scales, stream)
+
+
+def quantize_act_unrotated(x, act_bits: int = 4, codes=None, scales=None, stream=None):
+    """As quantize_act_h32 without the rotation."""
+    return _quantize("quantize_act_unrotated", x, act_bits, codes, scales, stream)
+
+
+def _gemm(name: str, codes, scales, act_bits, w, y, stream):
     torch = _torch()
     m = codes.shape[0]
     if y is None:
         y = torch.empty((m, w.n), dtype=torch.float32, device=codes.device)
-    st = _lib_handle().w4a4_gemm(_dptr(codes), _dptr(scales), act_bits, m,
-                                 ctypes.byref(w.desc), _dptr(w.image), _dptr(y), y.stride(0),
-                                 _stream_handle(stream))
-    _check(st, "w4a4_gemm")
+    st = getattr(_lib_handle(), name)(_dptr(codes), _dptr(scales), act_bits, m,
+                                      ctypes.byref(w.desc), _dptr(w.image), _dptr(y),
+                                      y.stride(0), _stream_handle(stream))
+    _check(st, name)
     return y
+
+
+def w4a4_gemm(codes, scales, act_bits: int, w: Weights, y=None, stream=None):
+    return _gemm("w4a4_gemm", codes, scales, act_bits, w, y, stream)
+
+
+def w4a4_gemm_unrotated(codes, scales, act_bits: int, w: Weights, y=None, stream=None):
+    """The product of the unrotated route (image from pack_weights_unrotated)."""
+    return _gemm("w4a4_gemm_unrotated", codes, scales, act_bits, w, y, stream)
 
 
 def w4a4_grouped_gemm(codes, scales, act_bits: int, expert_offsets, w: Weights, y=None,

@@ -75,10 +75,10 @@ bool shape_ok(int64_t n, int64_t k, int64_t e)
 // The stamp check: the analogue of refusing a file that is not a rotated one
 // ("509 tokens a second of prompt: the Hadamard route ships", section "Making
 // the file is part of the engine").
-bpg_status check_stamp(const bpg_weights_desc *w)
+bpg_status check_stamp(const bpg_weights_desc *w, uint32_t rotation = 32)
 {
     if (w->magic != BPG_WEIGHTS_MAGIC || w->version != BPG_WEIGHTS_VERSION ||
-        w->rotation != 32 || w->layout != BPG_LAYOUT_GROUP4)
+        w->rotation != rotation || w->layout != BPG_LAYOUT_GROUP4)
         return BPG_ERR_STAMP;
     if (!shape_ok(w->n, w->k, w->num_experts))
         return BPG_ERR_STAMP;
@@ -142,12 +142,13 @@ void rotate_block_f64(double v[32])
         v[i] = v[i] * c;
 }
 
-// One rotated Q4_0 block from 32 unrotated float weights.
-void quantize_weight_block(const double in[32], uint8_t blk[18])
+// One Q4_0 block from 32 unrotated float weights, rotated first if `rotate`.
+void quantize_weight_block(const double in[32], bool rotate, uint8_t blk[18])
 {
     double v[32];
     std::memcpy(v, in, sizeof v);
-    rotate_block_f64(v);
+    if (rotate)
+        rotate_block_f64(v);
     double amax = 0.0;
     for (int i = 0; i < 32; i++)
         amax = std::fabs(v[i]) > amax ? std::fabs(v[i]) : amax;
@@ -191,7 +192,7 @@ const char *bpg_status_str(bpg_status s)
     case BPG_ERR_SHAPE: return "invalid shape";
     case BPG_ERR_ALIGN: return "misaligned pointer or leading dimension";
     case BPG_ERR_DTYPE: return "unsupported dtype, source kind or act_bits";
-    case BPG_ERR_STAMP: return "weight image stamp missing, foreign, unrotated or inconsistent";
+    case BPG_ERR_STAMP: return "weight image stamp missing, foreign, of the other route or inconsistent";
     case BPG_ERR_BUFFER: return "destination buffer too small";
     case BPG_ERR_DEVICE: return "current device is not a gfx950 GPU";
     case BPG_ERR_LAUNCH: return "kernel launch failed";
@@ -206,11 +207,20 @@ size_t rotate_pack_weights_bytes(int64_t n, int64_t k, int64_t num_experts)
     return (size_t)image_bytes(n, k, num_experts);
 }
 
-bpg_status rotate_pack_weights(const void *src, bpg_src_kind kind, int64_t n, int64_t k,
-                               int64_t num_experts, void *dst_host, size_t dst_bytes,
-                               bpg_weights_desc *desc_out)
+} // extern "C"
+
+namespace {
+
+// The packer of both routes: `rotate` selects the rotated image (stamp
+// rotation 32; sources: float weights, rotated on the way, or the Q4_0
+// tensors of a rotated file) or the unrotated one (stamp rotation 0; sources:
+// float weights or plain Q4_0 tensors).
+bpg_status pack_image(const void *src, bpg_src_kind kind, int64_t n, int64_t k,
+                      int64_t num_experts, void *dst_host, size_t dst_bytes,
+                      bpg_weights_desc *desc_out, bool rotate)
 {
-    if (kind != BPG_SRC_F32 && kind != BPG_SRC_BF16 && kind != BPG_SRC_Q4_0_ROTATED)
+    const bpg_src_kind q4_kind = rotate ? BPG_SRC_Q4_0_ROTATED : BPG_SRC_Q4_0;
+    if (kind != BPG_SRC_F32 && kind != BPG_SRC_BF16 && kind != q4_kind)
         return BPG_ERR_DTYPE;
     if (!shape_ok(n, k, num_experts))
         return BPG_ERR_SHAPE;
@@ -232,7 +242,7 @@ bpg_status rotate_pack_weights(const void *src, bpg_src_kind kind, int64_t n, in
             for (int64_t b = 0; b < B; b++) {
                 uint8_t blk[18];
                 const int64_t row = e * n + r;
-                if (kind == BPG_SRC_Q4_0_ROTATED) {
+                if (kind == q4_kind) {
                     std::memcpy(blk, static_cast<const uint8_t *>(src) + (row * B + b) * 18, 18);
                 } else {
                     double in[32];
@@ -247,7 +257,7 @@ bpg_status rotate_pack_weights(const void *src, bpg_src_kind kind, int64_t n, in
                             in[i] = (double)f;
                         }
                     }
-                    quantize_weight_block(in, blk);
+                    quantize_weight_block(in, rotate, blk);
                 }
                 place_block(blk, e, r, b, n, G, img);
             }
@@ -256,7 +266,7 @@ bpg_status rotate_pack_weights(const void *src, bpg_src_kind kind, int64_t n, in
     std::memset(&d, 0, sizeof d);
     d.magic = BPG_WEIGHTS_MAGIC;
     d.version = BPG_WEIGHTS_VERSION;
-    d.rotation = 32;
+    d.rotation = rotate ? 32 : 0;
     d.layout = BPG_LAYOUT_GROUP4;
     d.n = n;
     d.k = k;
@@ -267,8 +277,8 @@ bpg_status rotate_pack_weights(const void *src, bpg_src_kind kind, int64_t n, in
     return BPG_OK;
 }
 
-bpg_status quantize_act_h32(const void *x, bpg_x_dtype dt, int64_t m, int64_t k, int64_t ldx,
-                            int act_bits, void *codes, float *scales, void *stream)
+bpg_status quantize_checked(const void *x, bpg_x_dtype dt, int64_t m, int64_t k, int64_t ldx,
+                            int act_bits, void *codes, float *scales, void *stream, int rotate)
 {
     if (dt != BPG_X_F32 && dt != BPG_X_BF16)
         return BPG_ERR_DTYPE;
@@ -284,17 +294,17 @@ bpg_status quantize_act_h32(const void *x, bpg_x_dtype dt, int64_t m, int64_t k,
     bpg_status s = check_device();
     if (s != BPG_OK)
         return s;
-    return launch_status(bpg::launch_quantize(x, (int)dt, m, k, ldx, act_bits, 1, codes, scales,
-                                              static_cast<hipStream_t>(stream)));
+    return launch_status(bpg::launch_quantize(x, (int)dt, m, k, ldx, act_bits, rotate, codes,
+                                              scales, static_cast<hipStream_t>(stream)));
 }
 
-bpg_status w4a4_gemm(const void *codes, const float *scales, int act_bits, int64_t m,
-                     const bpg_weights_desc *w, const void *w_dev, float *y, int64_t ldy,
-                     void *stream)
+bpg_status gemm_checked(const void *codes, const float *scales, int act_bits, int64_t m,
+                        const bpg_weights_desc *w, const void *w_dev, float *y, int64_t ldy,
+                        void *stream, uint32_t rotation)
 {
     if (!w)
         return BPG_ERR_NULL;
-    bpg_status s = check_stamp(w);
+    bpg_status s = check_stamp(w, rotation);
     if (s != BPG_OK)
         return s;
     if (w->num_experts != 1)
@@ -324,6 +334,51 @@ bpg_status w4a4_gemm(const void *codes, const float *scales, int act_bits, int64
     p.y = y;
     p.ldy = ldy;
     return launch_status(bpg::launch_gemm(p, static_cast<hipStream_t>(stream)));
+}
+
+} // namespace
+
+extern "C" {
+
+bpg_status rotate_pack_weights(const void *src, bpg_src_kind kind, int64_t n, int64_t k,
+                               int64_t num_experts, void *dst_host, size_t dst_bytes,
+                               bpg_weights_desc *desc_out)
+{
+    return pack_image(src, kind, n, k, num_experts, dst_host, dst_bytes, desc_out, true);
+}
+
+bpg_status pack_weights_unrotated(const void *src, bpg_src_kind kind, int64_t n, int64_t k,
+                                  int64_t num_experts, void *dst_host, size_t dst_bytes,
+                                  bpg_weights_desc *desc_out)
+{
+    return pack_image(src, kind, n, k, num_experts, dst_host, dst_bytes, desc_out, false);
+}
+
+bpg_status quantize_act_h32(const void *x, bpg_x_dtype dt, int64_t m, int64_t k, int64_t ldx,
+                            int act_bits, void *codes, float *scales, void *stream)
+{
+    return quantize_checked(x, dt, m, k, ldx, act_bits, codes, scales, stream, 1);
+}
+
+bpg_status quantize_act_unrotated(const void *x, bpg_x_dtype dt, int64_t m, int64_t k,
+                                  int64_t ldx, int act_bits, void *codes, float *scales,
+                                  void *stream)
+{
+    return quantize_checked(x, dt, m, k, ldx, act_bits, codes, scales, stream, 0);
+}
+
+bpg_status w4a4_gemm(const void *codes, const float *scales, int act_bits, int64_t m,
+                     const bpg_weights_desc *w, const void *w_dev, float *y, int64_t ldy,
+                     void *stream)
+{
+    return gemm_checked(codes, scales, act_bits, m, w, w_dev, y, ldy, stream, 32);
+}
+
+bpg_status w4a4_gemm_unrotated(const void *codes, const float *scales, int act_bits, int64_t m,
+                               const bpg_weights_desc *w, const void *w_dev, float *y,
+                               int64_t ldy, void *stream)
+{
+    return gemm_checked(codes, scales, act_bits, m, w, w_dev, y, ldy, stream, 0);
 }
 
 bpg_status w4a4_grouped_gemm(const void *codes, const float *scales, int act_bits,

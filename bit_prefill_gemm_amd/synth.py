@@ -72,6 +72,12 @@ def draw_q4_0(rng, rows_shape, k, d_lo, d_hi) -> np.ndarray:
     return blocks
 
 
+def draw_weights_f32(rng, rows, k, std) -> np.ndarray:
+    """Unquantized float weights [rows, k], normal with the given std (the
+    source of both offline packers in the route comparison)."""
+    return (rng.standard_normal((rows, k)) * std).astype(np.float32)
+
+
 def draw_routing(rng, tokens, experts, topk):
     """Return (token_of_row [tokens*topk], expert_of_row, offsets [experts+1] int32)."""
     choice = np.argsort(rng.random((tokens, experts)), axis=1)[:, :topk]

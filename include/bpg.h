@@ -59,19 +59,23 @@ typedef enum {
     BPG_ERR_SHAPE = 2,  /* a size is negative, K or N not a multiple of 32, ld too small, ... */
     BPG_ERR_ALIGN = 3,  /* a device pointer or leading dimension breaks the alignment rule */
     BPG_ERR_DTYPE = 4,  /* unknown dtype or source kind, or act_bits not 4 or 8 */
-    BPG_ERR_STAMP = 5,  /* weight descriptor not made by rotate_pack_weights, wrong
-                           version or layout, not rotated, or sizes that disagree */
+    BPG_ERR_STAMP = 5,  /* weight descriptor not made by this library's packers, wrong
+                           version or layout, an image of the other route (rotated
+                           vs unrotated), or sizes that disagree */
     BPG_ERR_BUFFER = 6, /* destination buffer too small */
     BPG_ERR_DEVICE = 7, /* the current device is not a gfx950 GPU */
     BPG_ERR_LAUNCH = 8  /* the kernel launch failed (hipGetLastError after enqueue) */
 } bpg_status;
 
-/* Source of rotate_pack_weights. */
+/* Source of rotate_pack_weights and pack_weights_unrotated. */
 typedef enum {
     BPG_SRC_F32 = 0,           /* unrotated float weights [E][N][K], fp32 */
     BPG_SRC_BF16 = 1,          /* unrotated float weights [E][N][K], bf16 bits */
-    BPG_SRC_Q4_0_ROTATED = 2   /* Q4_0 blocks [E][N][K/32] x 18 B of weights already
-                                  rotated by H32 (a rotated file's tensors) */
+    BPG_SRC_Q4_0_ROTATED = 2,  /* Q4_0 blocks [E][N][K/32] x 18 B of weights already
+                                  rotated by H32 (a rotated file's tensors);
+                                  rotate_pack_weights only */
+    BPG_SRC_Q4_0 = 3           /* plain (unrotated) Q4_0 blocks, same layout;
+                                  pack_weights_unrotated only */
 } bpg_src_kind;
 
 /* Activation dtype of quantize_act_h32. */
@@ -105,7 +109,8 @@ typedef enum { BPG_X_F32 = 0, BPG_X_BF16 = 1 } bpg_x_dtype;
 typedef struct {
     uint32_t magic;        /* BPG_WEIGHTS_MAGIC */
     uint32_t version;      /* BPG_WEIGHTS_VERSION */
-    uint32_t rotation;     /* 32: every block rotated by H32 */
+    uint32_t rotation;     /* 32: every block rotated by H32 (rotate_pack_weights);
+                              0: unrotated (pack_weights_unrotated) */
     uint32_t layout;       /* BPG_LAYOUT_GROUP4 */
     int64_t n;             /* output channels per expert */
     int64_t k;             /* input channels */
@@ -136,7 +141,8 @@ size_t rotate_pack_weights_bytes(int64_t n, int64_t k, int64_t num_experts);
  * Float sources are rotated per 32-block in fp64 (same butterfly order, times
  * fp64 1/sqrt(32)) and quantized to Q4_0: dw = fp16(amax/7), u = clamp(
  * rint(w'/dw), -8, 7) + 8 with the fp16-rounded dw.  Q4_0 sources are only
- * re-laid out.  Errors: NULL, SHAPE, DTYPE, BUFFER.
+ * re-laid out; plain BPG_SRC_Q4_0 is refused (DTYPE).  Errors: NULL, SHAPE,
+ * DTYPE, BUFFER.
  */
 bpg_status rotate_pack_weights(const void *src, bpg_src_kind kind, int64_t n, int64_t k,
                                int64_t num_experts, void *dst_host, size_t dst_bytes,
@@ -159,6 +165,37 @@ bpg_status rotate_pack_weights(const void *src, bpg_src_kind kind, int64_t n, in
  */
 bpg_status quantize_act_h32(const void *x, bpg_x_dtype dt, int64_t m, int64_t k, int64_t ldx,
                             int act_bits, void *codes, float *scales, void *stream);
+
+/*
+ * The unrotated W4A4 route ("Qwen3.8-27B at 45.7 tok/s: DFlash2 in 1bit serve,
+ * and 4-bit activations with a Hadamard rotation", section "Prompt processing:
+ * 4-bit activations, rotated first": plain Q4_0 weights read bit for bit and
+ * activations rounded to 4 bits with no rotation; faster to set up, larger
+ * error).  The same kernels run on an image and codes made without H32.
+ *
+ * pack_weights_unrotated: as rotate_pack_weights, but float sources are
+ * quantized to Q4_0 without rotation and BPG_SRC_Q4_0 blocks are only
+ * re-laid out; the stamp says rotation 0.  BPG_SRC_Q4_0_ROTATED is refused
+ * (DTYPE).  Errors: NULL, SHAPE, DTYPE, BUFFER.
+ *
+ * quantize_act_unrotated: as quantize_act_h32 with the rotation left out
+ * (amax, scale and codes of the raw 32-value blocks, same code layouts).
+ * Errors: NULL, SHAPE, ALIGN, DTYPE, DEVICE, LAUNCH.
+ *
+ * w4a4_gemm_unrotated: as w4a4_gemm, for codes from quantize_act_unrotated
+ * and an image stamped rotation 0 (a rotated image gives STAMP, and
+ * w4a4_gemm refuses an unrotated one the same way).
+ * Errors: NULL, SHAPE, ALIGN, DTYPE, STAMP, DEVICE, LAUNCH.
+ */
+bpg_status pack_weights_unrotated(const void *src, bpg_src_kind kind, int64_t n, int64_t k,
+                                  int64_t num_experts, void *dst_host, size_t dst_bytes,
+                                  bpg_weights_desc *desc_out);
+bpg_status quantize_act_unrotated(const void *x, bpg_x_dtype dt, int64_t m, int64_t k,
+                                  int64_t ldx, int act_bits, void *codes, float *scales,
+                                  void *stream);
+bpg_status w4a4_gemm_unrotated(const void *codes, const float *scales, int act_bits, int64_t m,
+                               const bpg_weights_desc *w, const void *w_dev, float *y,
+                               int64_t ldy, void *stream);
 
 /*
  * Dense W4A4 (or W4A8) product y = x . W^T from codes, on the GPU

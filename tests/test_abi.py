@@ -179,3 +179,63 @@ def test_binding_raises_typed_error():
     with pytest.raises(bb.BpgError) as ei:
         bb.rotate_pack_weights(np.zeros(10, dtype=np.uint8), 7, 64, 128)
     assert ei.value.status == DTYPE
+
+
+# ------------------------------------------------------------ unrotated route
+
+def gemm_u(desc=None, **kw):
+    d = desc if desc is not None else _desc_with(rotation=0)
+    a = dict(codes=P, scales=P2, bits=4, m=4, wdev=P, y=P2, ldy=64, stream=NUL)
+    a.update(kw)
+    return bb.lib().w4a4_gemm_unrotated(a["codes"], a["scales"], a["bits"], a["m"],
+                                        ctypes.byref(d), a["wdev"], a["y"], a["ldy"], a["stream"])
+
+
+def q_u(**kw):
+    a = dict(x=P, dt=0, m=4, k=128, ldx=128, bits=4, codes=P2, scales=P, stream=NUL)
+    a.update(kw)
+    return bb.lib().quantize_act_unrotated(a["x"], a["dt"], a["m"], a["k"], a["ldx"], a["bits"],
+                                           a["codes"], a["scales"], a["stream"])
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(desc=good_desc()), STAMP),                 # a rotated image is refused
+    (dict(desc=_desc_with(rotation=0, magic=3)), STAMP),
+    (dict(desc=_desc_with(rotation=0, bytes=5)), STAMP),
+    (dict(bits=5), DTYPE), (dict(ldy=32), SHAPE), (dict(y=NUL), NULL), (dict(y=MIS), ALIGN),
+])
+def test_unrotated_gemm_errors(kwargs, status):
+    assert gemm_u(**kwargs) == status
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(dt=5), DTYPE), (dict(bits=2), DTYPE), (dict(k=48, ldx=48), SHAPE),
+    (dict(x=NUL), NULL), (dict(codes=MIS), ALIGN),
+])
+def test_unrotated_quantize_errors(kwargs, status):
+    assert q_u(**kwargs) == status
+
+
+def test_unrotated_pack_errors_and_stamp():
+    lib = bb.lib()
+    d = bb.WeightsDesc()
+    src = np.zeros(64 * 4 * 18, dtype=np.uint8)
+    dst = np.zeros(64 * 4 * 18, dtype=np.uint8)
+    sp, dp = src.ctypes.data_as(ctypes.c_void_p), dst.ctypes.data_as(ctypes.c_void_p)
+    # each packer takes only its own route's Q4_0 tensors
+    assert lib.pack_weights_unrotated(sp, 2, 64, 128, 1, dp, dst.nbytes, ctypes.byref(d)) == DTYPE
+    assert lib.rotate_pack_weights(sp, 3, 64, 128, 1, dp, dst.nbytes, ctypes.byref(d)) == DTYPE
+    assert lib.pack_weights_unrotated(sp, 3, 64, 100, 1, dp, dst.nbytes, ctypes.byref(d)) == SHAPE
+    assert lib.pack_weights_unrotated(sp, 3, 64, 128, 1, NUL, dst.nbytes, ctypes.byref(d)) == NULL
+    assert lib.pack_weights_unrotated(sp, 3, 64, 128, 1, dp, 100, ctypes.byref(d)) == BUFFER
+    assert lib.pack_weights_unrotated(sp, 3, 64, 128, 1, dp, dst.nbytes, ctypes.byref(d)) == OK
+    assert d.rotation == 0 and d.layout == 3 and d.bytes == dst.nbytes
+    # the rotated route refuses the unrotated image, and blocksums / grouped do too
+    assert gemm(desc=d) == STAMP
+    assert sums(desc=d) == STAMP
+
+
+@pytest.mark.skipif(os.path.exists("/dev/kfd"), reason="host has a GPU driver")
+def test_unrotated_valid_calls_stop_at_device_check_without_gpu():
+    assert q_u() == DEVICE
+    assert gemm_u() == DEVICE

@@ -86,3 +86,31 @@ def test_float_source_reproduces_unrotated_product():
     y = oracle.ref_points(x, wq, dw, rows.ravel(), cols.ravel()).reshape(4, n)
     exact = x.astype(np.float64) @ w.astype(np.float64).T
     assert np.linalg.norm(y - exact) / np.linalg.norm(exact) < 0.1
+
+
+# ------------------------------------------------------------ unrotated route
+
+@pytest.mark.parametrize("n,k,e", [(32, 32, 1), (96, 160, 1), (64, 256, 2)])
+def test_unrotated_q4_0_source_is_relaid_out_verbatim(n, k, e):
+    blocks = synth.draw_q4_0(np.random.default_rng(5 * n + k + e), (e, n), k, 0.002, 0.02)
+    W = bb.pack_weights_unrotated(blocks, bb.SRC_Q4_0, n, k, e)
+    assert W.desc.rotation == 0 and W.desc.num_experts == e
+    assert np.array_equal(unpack_image(W.image, n, k, e), blocks)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_unrotated_float_source_matches_oracle_bit_exact(dtype):
+    rng = np.random.default_rng(23)
+    n, k, e = 64, 288, 2
+    w = synth.draw_weights_f32(rng, e * n, k, 0.03)
+    w[:, rng.choice(k, 5, replace=False)] *= 10.0
+    w[7, 96:128] = 0.0
+    src = w if dtype == "f32" else synth.bf16_bits(w)
+    kind = bb.SRC_F32 if dtype == "f32" else bb.SRC_BF16
+    W = bb.pack_weights_unrotated(src, kind, n, k, e)
+    got = unpack_image(W.image, n, k, e).reshape(e * n, k // 32, 18)
+    ref = oracle.quantize_weights_q4_0(src, rotate=False)
+    assert np.array_equal(got, ref)
+    # and the two routes differ: the rotated image holds other blocks
+    R = bb.rotate_pack_weights(src, kind, n, k, e)
+    assert not np.array_equal(unpack_image(R.image, n, k, e).reshape(e * n, k // 32, 18), got)
