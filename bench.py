@@ -70,7 +70,7 @@ WORKLOADS = {
 }
 # kernel sources of the GEMM paths (the tiled and grouped kernels, and the
 # weight-stream kernel used for a few rows)
-GEMM_SRCS = [os.path.join(ROOT, "bit_prefill_gemm_amd", "csrc", f) for f in ("gemm.hip", "skinny.hip")]
+GEMM_SRCS = [os.path.join(ROOT, "bit_prefill_gemm_amd", "csrc", f) for f in ("gemm.hip", "skinny.hip", "wide.hip", "operands.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_traffic.json")
 
 

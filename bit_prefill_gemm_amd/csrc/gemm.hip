@@ -38,16 +38,11 @@
 #include <type_traits>
 
 #include "internal.h"
+#include "operands.h"
 
 namespace bpg {
 
 namespace {
-
-typedef int v4i __attribute__((ext_vector_type(4)));
-typedef int v16i __attribute__((ext_vector_type(16)));
-
-constexpr int kMagicBits = 0x4B400000;
-constexpr float kMagic = 12582912.0f;
 
 enum Mode { kGemm = 0, kGrouped = 1, kSums = 2 };
 
@@ -93,25 +88,6 @@ struct Cfg {
     static_assert(kLds <= 160 * 1024, "LDS budget");
 };
 
-// Activation nibbles (two's complement) of one dword -> 8 int8 = 16 * value:
-// low nibbles first, then high nibbles.
-__device__ __forceinline__ uint32_t act_lo(uint32_t d) { return (d << 4) & 0xF0F0F0F0u; }
-__device__ __forceinline__ uint32_t act_hi(uint32_t d) { return d & 0xF0F0F0F0u; }
-// Q4_0 nibbles u -> top bit flipped (u XOR 8 is u-8 in two's complement) ->
-// 16*(u-8).
-__device__ __forceinline__ uint32_t q40_lo(uint32_t d) { return ((d << 4) ^ 0x80808080u) & 0xF0F0F0F0u; }
-__device__ __forceinline__ uint32_t q40_hi(uint32_t d) { return (d ^ 0x88888888u) & 0xF0F0F0F0u; }
-
-__device__ __forceinline__ long pack2(uint32_t lo, uint32_t hi)
-{
-    return (long)(((uint64_t)hi << 32) | lo);
-}
-
-__device__ __forceinline__ float half_bits_to_float(uint16_t h)
-{
-    return (float)__builtin_bit_cast(_Float16, h);
-}
-
 // LDS slot of activation row `r` of block `kc`: the low four bits are
 // XOR-swizzled so that both the staging writes (8 consecutive lanes write the
 // 8 blocks of one row, 16 lanes two rows) and the operand reads (consecutive
@@ -119,16 +95,6 @@ __device__ __forceinline__ float half_bits_to_float(uint16_t h)
 // group of 16.  Weight columns need none: their staging writes one dword
 // slot of 16 consecutive columns at a time.
 __device__ __forceinline__ int swz(int r, int kc) { return r ^ kc ^ ((r & 1) << 3); }
-
-// Workgroups are dispatched round-robin over the 8 XCDs (w % 8 selects the
-// XCD).  Hand each XCD a contiguous range of logical tiles, so tiles that
-// share weight columns share that XCD's L2.
-__device__ __forceinline__ int xcd_remap(int w, int total)
-{
-    if (total % 8 != 0)
-        return w;
-    return (w % 8) * (total / 8) + w / 8;
-}
 
 // Grouped tiling: expert e owns ceil(rows_e / BM) consecutive row slots.  Find
 // the expert and the row range of `slot` with a scan over the clamped offsets
@@ -206,41 +172,6 @@ __device__ __forceinline__ void with_count(int n, F &&f)
             with_count<N - 1>(n, f);
     }
 }
-
-// Operand and result registers of the two matrix instruction shapes.
-template <int MF> struct Mfma;
-
-template <> struct Mfma<16> {
-    typedef long Op;
-    typedef v4i Acc;
-    // lane l: row / column l % 16 of the tile and K group g = l / 16, which
-    // holds bytes 4g..4g+3 of the packed block (elements 4g..4g+3 from the
-    // low nibbles, 16+4g..16+4g+3 from the high ones); result register r of
-    // lane l is row 4g + r, column l % 16.
-    static __device__ __forceinline__ int rc(int lane) { return lane & 15; }
-    static __device__ __forceinline__ int kg(int lane) { return lane >> 4; }
-    static __device__ __forceinline__ int out_row(int g, int r) { return 4 * g + r; }
-    static __device__ __forceinline__ Acc mma(Op a, Op b, Acc c)
-    {
-        return __builtin_amdgcn_mfma_i32_16x16x32_i8(a, b, c, 0, 0, 0);
-    }
-};
-
-template <> struct Mfma<32> {
-    typedef v4i Op;
-    typedef v16i Acc;
-    // lane l: row / column l % 32 of the tile and K half g = l / 32, which
-    // holds bytes 8g..8g+7 of the packed block (elements 8g..8g+7 low,
-    // 16+8g..16+8g+7 high); result register r of lane l is row
-    // 8 (r / 4) + 4g + r % 4, column l % 32.
-    static __device__ __forceinline__ int rc(int lane) { return lane & 31; }
-    static __device__ __forceinline__ int kg(int lane) { return lane >> 5; }
-    static __device__ __forceinline__ int out_row(int g, int r) { return 8 * (r >> 2) + 4 * g + (r & 3); }
-    static __device__ __forceinline__ Acc mma(Op a, Op b, Acc c)
-    {
-        return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
-    }
-};
 
 template <class C, int MODE>
 __global__ __launch_bounds__(C::kThreads, C::kOcc) void w4a4_kernel(GemmProblem p, int tiles_m,
@@ -745,6 +676,9 @@ hipError_t launch_dense_bits(const GemmProblem &p, hipStream_t stream)
     for (int i = 0; i < 3; i++)
         if (e[i] < e[best])
             best = i;
+    // 4-bit activations: the wide shapes run the direct-load kernel (wide.hip)
+    if (BITS == 4 && best <= 1 && wide_fits(p, best == 0 ? 5 : 4))
+        return launch_wide(p, best == 0 ? 5 : 4, stream);
     switch (best) {
     case 0: return launch_dense_cfg<typename T::W64x160>(p, stream);
     case 1: return launch_dense_cfg<typename T::W64x128>(p, stream);

@@ -35,6 +35,10 @@ hipError_t launch_gemm(const GemmProblem &p, hipStream_t stream);
 // skinny_fits(p).
 bool skinny_fits(const GemmProblem &p);
 hipError_t launch_skinny(const GemmProblem &p, hipStream_t stream);
+// The wide-tile kernel (4-bit activations, dense, many rows): 64 x 32*tn
+// tiles, tn = 4 or 5; usable when wide_fits(p, tn).
+bool wide_fits(const GemmProblem &p, int tn);
+hipError_t launch_wide(const GemmProblem &p, int tn, hipStream_t stream);
 hipError_t launch_grouped_gemm(const GemmProblem &p, hipStream_t stream);
 hipError_t launch_blocksums(const GemmProblem &p, hipStream_t stream);
 

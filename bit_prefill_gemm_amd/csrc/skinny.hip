@@ -31,15 +31,11 @@
 #include <stdint.h>
 
 #include "internal.h"
+#include "operands.h"
 
 namespace bpg {
 
 namespace {
-
-typedef int v4i __attribute__((ext_vector_type(4)));
-
-constexpr int kMagicBits = 0x4B400000;
-constexpr float kMagic = 12582912.0f;
 
 template <int BITS_, int TM_, int NW_, int TN_, int D_>
 struct SkCfg {
@@ -60,16 +56,6 @@ struct SkCfg {
     static constexpr int kR = TM * TN * 4;            // accumulators per lane
     static constexpr int kLdsRed = NW * kR * 64 * 4;  // bytes for the final reduction
 };
-
-__device__ __forceinline__ uint32_t act_lo(uint32_t d) { return (d << 4) & 0xF0F0F0F0u; }
-__device__ __forceinline__ uint32_t act_hi(uint32_t d) { return d & 0xF0F0F0F0u; }
-__device__ __forceinline__ uint32_t q40_lo(uint32_t d) { return ((d << 4) ^ 0x80808080u) & 0xF0F0F0F0u; }
-__device__ __forceinline__ uint32_t q40_hi(uint32_t d) { return (d ^ 0x88888888u) & 0xF0F0F0F0u; }
-
-__device__ __forceinline__ long pack2(uint32_t lo, uint32_t hi)
-{
-    return (long)(((uint64_t)hi << 32) | lo);
-}
 
 // The same address in every lane, made visibly uniform (scalar registers).
 typedef const __attribute__((address_space(1))) uint8_t *gptr;
@@ -223,7 +209,7 @@ __global__ __launch_bounds__(C::kThreads) void skinny_kernel(GemmProblem p)
             for (int j = 0; j < TN; j++) {
                 const uint32_t hp = j == 0 ? (q < 2 ? rdw[d].x : rdw[d].y) : (q < 2 ? rdw[d].z : rdw[d].w);
                 const uint16_t hb = (uint16_t)((q & 1) ? hp >> 16 : hp & 0xFFFFu);
-                const float dw = (float)__builtin_bit_cast(_Float16, hb);
+                const float dw = half_bits_to_float(hb);
                 const float cm = -kMagic * dw; // exact: dw has 11 significant bits
 #pragma unroll
                 for (int i = 0; i < TM; i++) {
