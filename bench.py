@@ -19,8 +19,8 @@ Prints ONE JSON line.  `value` is prompt tokens per second of the step.  The
 `roofline` object covers the GEMM kernel (the dominant kernel).  Its average
 duration is measured with HIP events recorded on the launch stream around
 every GEMM in the timed region.  With many rows the kernel is bound by its
-fp32 VALU epilogue (two VALU operations per output element and 32-block), so
-the roofline is taken against the VALU issue rate; the int8 matrix-core view
+fp32 VALU epilogue (two FMAs per output element and 32-block), so the
+roofline is taken against the fp32 vector peak; the int8 matrix-core view
 (effective TOPS against the dense int8 peak) is reported beside it.  With 32
 rows or fewer it is bound by the weight stream: the roofline is HBM bytes per
 second against the HBM peak.
@@ -51,9 +51,10 @@ if ROOT not in sys.path:
 # MI355X published peaks
 PEAK_INT8_OPS = 5.0e15                    # dense int8 matrix ops/s
 PEAK_HBM = 8.0e12                         # bytes/s
-# fp32 VALU issue rate with packed fp32 instructions unused:
-# 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz
-PEAK_VALU_OPS = 256 * 4 * 16 * 2.4e9      # 39.3e12 lane-operations/s
+# fp32 vector peak: 256 CUs x 4 SIMDs x 32 lanes x 2 flops (one FMA) x 2.4 GHz.
+# gfx950 issues a non-packed wave64 FMA in two cycles, so this peak applies to
+# the plain fp32 FMAs of the epilogue (a pure FMA loop measures ~125 TFLOP/s).
+PEAK_FP32_FLOPS = 157.3e12
 
 WORKLOADS = {
     "attn512": dict(m=512, k=5120, n=5120),
@@ -236,7 +237,7 @@ def main():
     gemm_s = gemm_ms * 1e-3
     ops = 2.0 * m * n * k
     eff_tops = ops / gemm_s / 1e12
-    epi_ops = 2.0 * m * n * (k // 32)     # algorithmic fp32 VALU lane-operations
+    epi_flops = 4.0 * m * n * (k // 32)   # algorithmic: two fp32 FMAs per output and block
     gbytes = gemm_bytes(m, k, n, bits, experts)
     traffic = measured_traffic(args.workload, bits)
 
@@ -248,9 +249,9 @@ def main():
                     "kernel": kernel}
     else:
         # the fp32 epilogue (two VALU operations per output and block) binds
-        roofline = {"bound": "alu", "achieved": epi_ops / gemm_s / 1e12,
-                    "peak": PEAK_VALU_OPS / 1e12, "unit": "T fp32 VALU lane-op/s",
-                    "frac": epi_ops / gemm_s / PEAK_VALU_OPS, "traffic": traffic,
+        roofline = {"bound": "alu", "achieved": epi_flops / gemm_s / 1e12,
+                    "peak": PEAK_FP32_FLOPS / 1e12, "unit": "TFLOP/s",
+                    "frac": epi_flops / gemm_s / PEAK_FP32_FLOPS, "traffic": traffic,
                     "kernel": kernel}
 
     out = {
