@@ -65,6 +65,10 @@ def _load():
         "orc_grouped_points": (None, [_p, _p, _p, _i64, _p, _p, _i64, _i64, _p, _p, _i64, _p]),
         "orc_ref_points": (None, [_p, ctypes.c_int, _i64, _p, _p, _i64, _p, _p, _i64, _p]),
         "orc_num_threads": (ctypes.c_int, []),
+        "orc_exp_f32": (ctypes.c_float, [ctypes.c_float]),
+        "orc_silu_f32": (ctypes.c_float, [ctypes.c_float]),
+        "orc_swiglu_quantize": (_i64, [_p, _i64, _i64, _i64, ctypes.c_int, _p, _p]),
+        "orc_moe_combine": (None, [_p, _i64, _p, _p, _i64, _i64, _i64, _p, _i64]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -240,3 +244,60 @@ def ref_points(x, w, dw, rows, cols) -> np.ndarray:
 
 def num_threads() -> int:
     return int(_load().orc_num_threads())
+
+
+# ---------------------------------------------------------------- MoE glue
+
+def exp_f32(x: np.ndarray) -> np.ndarray:
+    """The fp32 exponential of the SwiGLU reading (elementwise)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    f = _load().orc_exp_f32
+    return np.array([f(float(v)) for v in x.ravel()], dtype=np.float32).reshape(x.shape)
+
+
+def silu_f32(g: np.ndarray) -> np.ndarray:
+    g = np.ascontiguousarray(g, dtype=np.float32)
+    f = _load().orc_silu_f32
+    return np.array([f(float(v)) for v in g.ravel()], dtype=np.float32).reshape(g.shape)
+
+
+def swiglu_quantize(gu: np.ndarray, inter: int, bits: int = 4):
+    """gu: fp32 [rows, >= 2 inter] (gate then up).  Returns (q, d, ties) as quantize()."""
+    gu = np.ascontiguousarray(gu, dtype=np.float32)
+    rows, ld = gu.shape
+    assert inter % 32 == 0 and ld >= 2 * inter and bits in (4, 8)
+    q = np.empty((rows, inter), dtype=np.int8)
+    d = np.empty((rows, inter // 32), dtype=np.float32)
+    ties = _load().orc_swiglu_quantize(_ptr(gu), rows, inter, ld, bits, _ptr(q), _ptr(d))
+    return q, d, int(ties)
+
+
+def route_sort(expert_of: np.ndarray, experts: int):
+    """Expert-sorted order of routed rows (token t, choice j) -> entry t*k + j.
+
+    Stable by (expert, entry).  Returns (offsets int32 [E+1], row_entry int32
+    [N]: the entry at each sorted position, slot_of int32 [N]: the sorted
+    position of each entry)."""
+    e = np.ascontiguousarray(expert_of, dtype=np.int64).ravel()
+    assert e.size == 0 or (e.min() >= 0 and e.max() < experts)
+    order = np.argsort(e, kind="stable")
+    counts = np.bincount(e, minlength=experts)
+    offsets = np.zeros(experts + 1, dtype=np.int32)
+    offsets[1:] = np.cumsum(counts)
+    slot_of = np.empty(e.size, dtype=np.int32)
+    slot_of[order] = np.arange(e.size, dtype=np.int32)
+    return offsets, order.astype(np.int32), slot_of
+
+
+def moe_combine(dn: np.ndarray, slot_of: np.ndarray, weights: np.ndarray, tokens: int,
+                topk: int) -> np.ndarray:
+    dn = np.ascontiguousarray(dn, dtype=np.float32)
+    slot = np.ascontiguousarray(slot_of, dtype=np.int32)
+    w = np.ascontiguousarray(weights, dtype=np.float32)
+    assert slot.size == tokens * topk and w.size == tokens * topk
+    assert slot.size == 0 or (slot.min() >= 0 and slot.max() < dn.shape[0])
+    hidden = dn.shape[1]
+    out = np.empty((tokens, hidden), dtype=np.float32)
+    _load().orc_moe_combine(_ptr(dn), dn.shape[1], _ptr(slot), _ptr(w), tokens, topk, hidden,
+                            _ptr(out), hidden)
+    return out

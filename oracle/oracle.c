@@ -429,6 +429,97 @@ void orc_ref_points(const void *x, int dtype, int64_t ldx, const int8_t *w, cons
     }
 }
 
+/* ------------------------------------------------------------------ */
+/* MoE glue around the grouped product [MOE "4-bit activations reach   */
+/* the MoE experts": the route covers the expert matmuls].  The pages   */
+/* give no detail of the rest of the expert layer; the readings here    */
+/* are: h = silu(gate) * up feeds the down projection and is rotated    */
+/* and quantized like any activation, and the routed rows are combined  */
+/* by their routing weights in a fixed order.                           */
+/* ------------------------------------------------------------------ */
+
+/*
+ * e^x in fp32, every step one correctly rounded fp32 operation (no FMA):
+ * Cody-Waite range reduction n = rint(x log2 e), r = (x - n ln2_hi) - n ln2_lo
+ * (ln2_hi has 16 significant bits, so n ln2_hi is exact for |n| <= 128),
+ * then the degree-6 Taylor polynomial of e^r in Horner form and a scaling by
+ * 2^n.  |r| <= ln2/2, where the truncation error is below 1.4e-7 relative.
+ * x is clamped to [-87, 88], which keeps 2^n and the result normal.
+ */
+float orc_exp_f32(float x)
+{
+    if (x < -87.0f)
+        x = -87.0f;
+    if (x > 88.0f)
+        x = 88.0f;
+    const float log2e = (float)1.4426950408889634;
+    const float ln2_hi = 0.693145751953125f;
+    const float ln2_lo = (float)(0.6931471805599453 - 0.693145751953125);
+    const float n = rintf(x * log2e);
+    const float r = (x - n * ln2_hi) - n * ln2_lo;
+    float p = 1.0f / 720.0f;
+    p = p * r + 1.0f / 120.0f;
+    p = p * r + 1.0f / 24.0f;
+    p = p * r + 1.0f / 6.0f;
+    p = p * r + 0.5f;
+    p = p * r + 1.0f;
+    p = p * r + 1.0f;
+    return ldexpf(p, (int)n);
+}
+
+/* silu(g) = g / (1 + e^-g), fp32, IEEE division. */
+float orc_silu_f32(float g)
+{
+    const float e = orc_exp_f32(-g);
+    const float den = 1.0f + e;
+    return g / den;
+}
+
+/*
+ * gu: [rows][ld] fp32, the gate projection in columns [0, inter) and the up
+ * projection in columns [inter, 2 inter).  h = silu(gate) * up (one fp32
+ * multiply), then h is rotated and quantized exactly as orc_quantize does
+ * with rotate = 1.  q: [rows][inter] codes, d: [rows][inter/32] scales.
+ */
+int64_t orc_swiglu_quantize(const float *gu, int64_t rows, int64_t inter, int64_t ld, int bits,
+                            int8_t *q, float *d)
+{
+    const int64_t nb = inter / QK;
+    int64_t ties = 0;
+#pragma omp parallel for reduction(+ : ties) schedule(static)
+    for (int64_t r = 0; r < rows; r++) {
+        for (int64_t b = 0; b < nb; b++) {
+            float h[QK], v[QK];
+            for (int i = 0; i < QK; i++) {
+                const float g = gu[r * ld + b * QK + i];
+                const float u = gu[r * ld + inter + b * QK + i];
+                h[i] = orc_silu_f32(g) * u;
+            }
+            orc_rotate_f32(h, v, 1);
+            ties += quantize_block(v, bits, q + r * inter + b * QK, d + r * nb + b);
+        }
+    }
+    return ties;
+}
+
+/*
+ * Weighted combine of the routed rows: out[t][c] = sum_j w[t k + j] *
+ * dn[slot[t k + j]][c] for j = 0 .. k-1 in that order, the accumulator
+ * starting at 0 and every step one fp32 fma.
+ */
+void orc_moe_combine(const float *dn, int64_t lddn, const int32_t *slot, const float *w,
+                     int64_t tokens, int64_t topk, int64_t hidden, float *out, int64_t ldo)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < tokens; t++)
+        for (int64_t c = 0; c < hidden; c++) {
+            float acc = 0.0f;
+            for (int64_t j = 0; j < topk; j++)
+                acc = fmaf(w[t * topk + j], dn[(int64_t)slot[t * topk + j] * lddn + c], acc);
+            out[t * ldo + c] = acc;
+        }
+}
+
 int orc_num_threads(void)
 {
 #ifdef _OPENMP
