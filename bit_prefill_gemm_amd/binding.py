@@ -25,7 +25,8 @@ X_F32, X_BF16 = 0, 1
 
 ENTRY_POINTS = ("bpg_status_str", "rotate_pack_weights_bytes", "rotate_pack_weights",
                 "quantize_act_h32", "w4a4_gemm", "w4a4_grouped_gemm", "w4a4_gemm_blocksums",
-                "pack_weights_unrotated", "quantize_act_unrotated", "w4a4_gemm_unrotated")
+                "pack_weights_unrotated", "quantize_act_unrotated", "w4a4_gemm_unrotated",
+                "moe_route_sort", "w4a4_grouped_gemm_gather", "swiglu_quantize_h32", "moe_combine")
 
 
 class WeightsDesc(ctypes.Structure):
@@ -76,6 +77,15 @@ def _lib_handle():
     lib.w4a4_grouped_gemm.restype = ctypes.c_int
     lib.w4a4_grouped_gemm.argtypes = [_vp, _vp, ctypes.c_int, _i64, _vp,
                                       ctypes.POINTER(WeightsDesc), _vp, _vp, _i64, _vp]
+    lib.moe_route_sort.restype = ctypes.c_int
+    lib.moe_route_sort.argtypes = [_vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp]
+    lib.w4a4_grouped_gemm_gather.restype = ctypes.c_int
+    lib.w4a4_grouped_gemm_gather.argtypes = [_vp, _vp, ctypes.c_int, _i64, _vp, _i64, _vp,
+                                             ctypes.POINTER(WeightsDesc), _vp, _vp, _i64, _vp]
+    lib.swiglu_quantize_h32.restype = ctypes.c_int
+    lib.swiglu_quantize_h32.argtypes = [_vp, _i64, _i64, _i64, ctypes.c_int, _vp, _vp, _vp]
+    lib.moe_combine.restype = ctypes.c_int
+    lib.moe_combine.argtypes = [_vp, _i64, _i64, _vp, _vp, _i64, _i64, _i64, _vp, _i64, _vp]
     lib.w4a4_gemm_blocksums.restype = ctypes.c_int
     lib.w4a4_gemm_blocksums.argtypes = [_vp, _vp, ctypes.c_int, _i64,
                                         ctypes.POINTER(WeightsDesc), _vp, _i64, _i64, _i64, _i64,
@@ -245,3 +255,64 @@ def w4a4_gemm_blocksums(codes, scales, act_bits: int, w: Weights, m0: int, m1: i
                                            n0, n1, _dptr(sums), _stream_handle(stream))
     _check(st, "w4a4_gemm_blocksums")
     return sums
+
+
+# ------------------------------------------------------------------ expert layer glue
+
+def moe_route_sort(expert_of, tokens: int, topk: int, experts: int, stream=None):
+    """expert_of: cuda int32 [tokens*topk].  Returns (offsets [E+1], row_token, slot_of)."""
+    torch = _torch()
+    n = tokens * topk
+    dev = expert_of.device
+    offsets = torch.empty(experts + 1, dtype=torch.int32, device=dev)
+    row_token = torch.empty(n, dtype=torch.int32, device=dev)
+    slot_of = torch.empty(n, dtype=torch.int32, device=dev)
+    st = _lib_handle().moe_route_sort(_dptr(expert_of), tokens, topk, experts, _dptr(offsets),
+                                      _dptr(row_token), _dptr(slot_of), _stream_handle(stream))
+    _check(st, "moe_route_sort")
+    return offsets, row_token, slot_of
+
+
+def w4a4_grouped_gemm_gather(codes, scales, act_bits: int, row_ids, expert_offsets, w: Weights,
+                             y=None, stream=None):
+    torch = _torch()
+    src_rows = codes.shape[0]
+    rows = row_ids.shape[0]
+    if y is None:
+        y = torch.empty((rows, w.n), dtype=torch.float32, device=codes.device)
+    st = _lib_handle().w4a4_grouped_gemm_gather(_dptr(codes), _dptr(scales), act_bits, src_rows,
+                                                _dptr(row_ids), rows, _dptr(expert_offsets),
+                                                ctypes.byref(w.desc), _dptr(w.image), _dptr(y),
+                                                y.stride(0), _stream_handle(stream))
+    _check(st, "w4a4_grouped_gemm_gather")
+    return y
+
+
+def swiglu_quantize_h32(gu, inter: int, act_bits: int = 4, codes=None, scales=None, stream=None):
+    """gu: cuda fp32 [rows, >= 2*inter] (gate then up).  Returns (codes, scales)."""
+    torch = _torch()
+    if gu.dim() != 2 or gu.stride(1) != 1 or gu.dtype != torch.float32:
+        raise ValueError("gu must be a 2-D float32 tensor with unit stride along columns")
+    rows = gu.shape[0]
+    if codes is None:
+        codes = torch.empty((rows, inter // 2 if act_bits == 4 else inter), dtype=torch.uint8,
+                            device=gu.device)
+    if scales is None:
+        scales = torch.empty((rows, inter // 32), dtype=torch.float32, device=gu.device)
+    st = _lib_handle().swiglu_quantize_h32(_dptr(gu), rows, inter, gu.stride(0), act_bits,
+                                           _dptr(codes), _dptr(scales), _stream_handle(stream))
+    _check(st, "swiglu_quantize_h32")
+    return codes, scales
+
+
+def moe_combine(dn, slot_of, weights, tokens: int, topk: int, y=None, stream=None):
+    """dn: cuda fp32 [rows, hidden] (sorted rows).  Returns y [tokens, hidden]."""
+    torch = _torch()
+    rows, hidden = dn.shape
+    if y is None:
+        y = torch.empty((tokens, hidden), dtype=torch.float32, device=dn.device)
+    st = _lib_handle().moe_combine(_dptr(dn), dn.stride(0), rows, _dptr(slot_of), _dptr(weights),
+                                   tokens, topk, hidden, _dptr(y), y.stride(0),
+                                   _stream_handle(stream))
+    _check(st, "moe_combine")
+    return y

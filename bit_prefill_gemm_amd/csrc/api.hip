@@ -42,6 +42,10 @@ bpg_status check_device()
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// expert sort: one workgroup, LDS of (1 + 16) ints per expert
+constexpr int64_t kMaxSortExperts = 512;
+constexpr int64_t kMaxSortEntries = (int64_t)1 << 24;
+
 bpg_status launch_status(hipError_t e) { return e == hipSuccess ? BPG_OK : BPG_ERR_LAUNCH; }
 
 // groups of four blocks per row
@@ -381,25 +385,45 @@ bpg_status w4a4_gemm_unrotated(const void *codes, const float *scales, int act_b
     return gemm_checked(codes, scales, act_bits, m, w, w_dev, y, ldy, stream, 0);
 }
 
-bpg_status w4a4_grouped_gemm(const void *codes, const float *scales, int act_bits,
-                             int64_t total_rows, const int32_t *expert_offsets_dev,
-                             const bpg_weights_desc *w, const void *w_dev, float *y,
-                             int64_t ldy, void *stream)
+} // extern "C"
+
+namespace {
+
+// gather: rows are read through row_ids (src_rows activation rows)
+bpg_status grouped_checked(const void *codes, const float *scales, int act_bits, bool gather,
+                           int64_t src_rows, const int32_t *row_ids, int64_t total_rows,
+                           const int32_t *expert_offsets_dev, const bpg_weights_desc *w,
+                           const void *w_dev, float *y, int64_t ldy, void *stream)
 {
     if (!w)
         return BPG_ERR_NULL;
     bpg_status s = check_stamp(w);
     if (s != BPG_OK)
         return s;
-    s = check_act(codes, scales, act_bits, total_rows, w->k);
+    if (total_rows < 0 || total_rows > ((int64_t)1 << 31) - 1)
+        return BPG_ERR_SHAPE;
+    s = check_act(codes, scales, act_bits, gather ? src_rows : total_rows, w->k);
     if (s != BPG_OK)
         return s;
+    if (gather) {
+        if (src_rows < 0)
+            return BPG_ERR_SHAPE;
+        if (total_rows > 0 && !row_ids)
+            return BPG_ERR_NULL;
+        // gathered rows are addressed from row 0 with 32-bit offsets
+        const int64_t row_bytes = w->k * (act_bits == 4 ? 16 : 32) / 32;
+        if (total_rows > 0 && src_rows == 0)
+            return BPG_ERR_SHAPE;
+        if (src_rows * row_bytes >= ((int64_t)1 << 31) || src_rows * (w->k / 32) >= ((int64_t)1 << 31))
+            return BPG_ERR_SHAPE;
+    }
     if (ldy < w->n)
         return BPG_ERR_SHAPE;
     if (!w_dev || !expert_offsets_dev || (total_rows > 0 && !y))
         return BPG_ERR_NULL;
     if (!aligned16(w_dev) || !aligned16(y) || ldy % 4 != 0 ||
-        (reinterpret_cast<uintptr_t>(expert_offsets_dev) & 3u) != 0)
+        (reinterpret_cast<uintptr_t>(expert_offsets_dev) & 3u) != 0 ||
+        (reinterpret_cast<uintptr_t>(row_ids) & 3u) != 0)
         return BPG_ERR_ALIGN;
     s = check_device();
     if (s != BPG_OK)
@@ -417,7 +441,92 @@ bpg_status w4a4_grouped_gemm(const void *codes, const float *scales, int act_bit
     p.y = y;
     p.ldy = ldy;
     p.offsets = expert_offsets_dev;
+    p.row_ids = gather ? row_ids : nullptr;
+    p.src_rows = src_rows;
     return launch_status(bpg::launch_grouped_gemm(p, static_cast<hipStream_t>(stream)));
+}
+
+} // namespace
+
+extern "C" {
+
+bpg_status w4a4_grouped_gemm(const void *codes, const float *scales, int act_bits,
+                             int64_t total_rows, const int32_t *expert_offsets_dev,
+                             const bpg_weights_desc *w, const void *w_dev, float *y,
+                             int64_t ldy, void *stream)
+{
+    return grouped_checked(codes, scales, act_bits, false, total_rows, nullptr, total_rows,
+                           expert_offsets_dev, w, w_dev, y, ldy, stream);
+}
+
+bpg_status w4a4_grouped_gemm_gather(const void *codes, const float *scales, int act_bits,
+                                    int64_t src_rows, const int32_t *row_ids_dev,
+                                    int64_t total_rows, const int32_t *expert_offsets_dev,
+                                    const bpg_weights_desc *w, const void *w_dev, float *y,
+                                    int64_t ldy, void *stream)
+{
+    return grouped_checked(codes, scales, act_bits, true, src_rows, row_ids_dev, total_rows,
+                           expert_offsets_dev, w, w_dev, y, ldy, stream);
+}
+
+bpg_status moe_route_sort(const int32_t *expert_of_dev, int64_t tokens, int64_t topk,
+                          int64_t experts, int32_t *offsets_dev, int32_t *row_token_dev,
+                          int32_t *slot_of_dev, void *stream)
+{
+    if (tokens < 0 || topk < 1 || experts < 1 || experts > kMaxSortExperts ||
+        tokens * topk > kMaxSortEntries)
+        return BPG_ERR_SHAPE;
+    if (!offsets_dev || (tokens > 0 && (!expert_of_dev || !row_token_dev || !slot_of_dev)))
+        return BPG_ERR_NULL;
+    if (((reinterpret_cast<uintptr_t>(expert_of_dev) | reinterpret_cast<uintptr_t>(offsets_dev) |
+          reinterpret_cast<uintptr_t>(row_token_dev) | reinterpret_cast<uintptr_t>(slot_of_dev)) &
+         3u) != 0)
+        return BPG_ERR_ALIGN;
+    bpg_status s = check_device();
+    if (s != BPG_OK)
+        return s;
+    return launch_status(bpg::launch_route_sort(expert_of_dev, tokens, topk, experts, offsets_dev,
+                                                row_token_dev, slot_of_dev,
+                                                static_cast<hipStream_t>(stream)));
+}
+
+bpg_status swiglu_quantize_h32(const float *gu, int64_t rows, int64_t inter, int64_t ldgu,
+                               int act_bits, void *codes, float *scales, void *stream)
+{
+    if (act_bits != 4 && act_bits != 8)
+        return BPG_ERR_DTYPE;
+    if (rows < 0 || inter <= 0 || inter % 32 != 0 || ldgu < 2 * inter ||
+        rows > ((int64_t)1 << 31) - 1 || inter > ((int64_t)1 << 30) || ldgu > ((int64_t)1 << 40))
+        return BPG_ERR_SHAPE;
+    if (rows > 0 && (!gu || !codes || !scales))
+        return BPG_ERR_NULL;
+    if (!aligned16(gu) || !aligned16(codes) || !aligned16(scales) || ldgu % 4 != 0)
+        return BPG_ERR_ALIGN;
+    bpg_status s = check_device();
+    if (s != BPG_OK)
+        return s;
+    return launch_status(bpg::launch_swiglu_quantize(gu, rows, inter, ldgu, act_bits, codes, scales,
+                                                     static_cast<hipStream_t>(stream)));
+}
+
+bpg_status moe_combine(const float *dn, int64_t lddn, int64_t rows, const int32_t *slot_of_dev,
+                       const float *weights_dev, int64_t tokens, int64_t topk, int64_t hidden,
+                       float *y, int64_t ldy, void *stream)
+{
+    if (tokens < 0 || topk < 1 || hidden <= 0 || hidden % 4 != 0 || lddn < hidden ||
+        ldy < hidden || rows < 0 || (tokens > 0 && rows == 0) || tokens * topk > kMaxSortEntries)
+        return BPG_ERR_SHAPE;
+    if (tokens > 0 && (!dn || !slot_of_dev || !weights_dev || !y))
+        return BPG_ERR_NULL;
+    if (!aligned16(dn) || !aligned16(y) || lddn % 4 != 0 || ldy % 4 != 0 ||
+        ((reinterpret_cast<uintptr_t>(slot_of_dev) | reinterpret_cast<uintptr_t>(weights_dev)) &
+         3u) != 0)
+        return BPG_ERR_ALIGN;
+    bpg_status s = check_device();
+    if (s != BPG_OK)
+        return s;
+    return launch_status(bpg::launch_combine(dn, lddn, rows, slot_of_dev, weights_dev, tokens, topk,
+                                             hidden, y, ldy, static_cast<hipStream_t>(stream)));
 }
 
 bpg_status w4a4_gemm_blocksums(const void *codes, const float *scales, int act_bits, int64_t m,

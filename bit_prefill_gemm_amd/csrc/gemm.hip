@@ -221,12 +221,22 @@ __global__ __launch_bounds__(C::kThreads, C::kOcc) void w4a4_kernel(GemmProblem 
     //      row_end are clamped to the last valid row: their values only reach
     //      output rows that are never stored.
     // (every offset below stays under 2^31 for K <= 2^22)
-    const uint8_t *__restrict__ a_base0 = p.codes + row0 * arow_bytes;
+    // Grouped rows may gather their activation rows through p.row_ids (the
+    // offsets are then taken from row 0; the host keeps src_rows * row bytes
+    // under 2^31).
+    const bool gather = MODE == kGrouped && p.row_ids != nullptr;
+    auto src_row = [&](int rrow) -> int64_t {
+        if (!gather)
+            return rrow;
+        const int64_t r = p.row_ids[row0 + rrow];
+        return r < 0 ? 0 : (r >= p.src_rows ? p.src_rows - 1 : r);
+    };
+    const uint8_t *__restrict__ a_base0 = p.codes + (gather ? 0 : row0) * arow_bytes;
     // weight image: 2304-byte blocks per (expert, 32-column tile, group of
     // four K-blocks): 2048 code bytes, then 128 fp16 scales (p.wscales points
     // at the first block's scales)
     const uint8_t *__restrict__ w_base0 = p.wcodes + (expert * ntiles32 + ct0) * NG * 2304;
-    const float *__restrict__ da_base0 = p.scales + row0 * B;
+    const float *__restrict__ da_base0 = p.scales + (gather ? 0 : row0) * B;
     const uint16_t *__restrict__ dw_base0 = p.wscales + (expert * ntiles32 + ct0) * NG * 1152;
     const int last_row = (int)(row_end - 1 - row0); // >= 0
 
@@ -241,7 +251,7 @@ __global__ __launch_bounds__(C::kThreads, C::kOcc) void w4a4_kernel(GemmProblem 
         const int rem = cc % (KC * (kAB / 16));
         const int kc = rem / (kAB / 16), part = rem % (kAB / 16);
         const int rrow = row < last_row ? row : last_row;
-        oa[i] = (uint32_t)(rrow * arow_bytes + kc * kAB + part * 16);
+        oa[i] = (uint32_t)(src_row(rrow) * arow_bytes + kc * kAB + part * 16);
         const int srow = swz(row, kc);
         // 8-bit codes: the two 16-byte halves of a row block swap places on
         // every other group of 8 rows (reads of 16 rows then avoid conflicts)
@@ -266,7 +276,7 @@ __global__ __launch_bounds__(C::kThreads, C::kOcc) void w4a4_kernel(GemmProblem 
         const int cc = c < BM * KC ? c : 0;
         const int kc = cc / BM, row = cc % BM;
         const int rrow = row < last_row ? row : last_row;
-        oda[i] = (uint32_t)(rrow * B + kc);
+        oda[i] = (uint32_t)(src_row(rrow) * B + kc);
         lda_[i] = (uint32_t)(kc * BM + row);
         kcda[i] = (int8_t)(c < BM * KC ? kc : 127);
     }

@@ -11,6 +11,17 @@ namespace bpg {
 hipError_t launch_quantize(const void *x, int dtype, int64_t m, int64_t k, int64_t ldx,
                            int act_bits, int rotate, void *codes, float *scales,
                            hipStream_t stream);
+// h = silu(gate) * up from gu [rows][ldgu] (gate: columns [0, inter), up:
+// [inter, 2 inter)), then rotation + quantization of h.
+hipError_t launch_swiglu_quantize(const float *gu, int64_t rows, int64_t inter, int64_t ldgu,
+                                  int act_bits, void *codes, float *scales, hipStream_t stream);
+// Expert sort of routed rows and the weighted combine (moe.hip).
+hipError_t launch_route_sort(const int32_t *expert_of, int64_t tokens, int64_t topk,
+                             int64_t experts, int32_t *offsets, int32_t *row_token,
+                             int32_t *slot_of, hipStream_t stream);
+hipError_t launch_combine(const float *dn, int64_t lddn, int64_t rows, const int32_t *slot_of,
+                          const float *weights, int64_t tokens, int64_t topk, int64_t hidden,
+                          float *y, int64_t ldy, hipStream_t stream);
 
 // Arguments common to the dense, grouped and block-sum launches.
 struct GemmProblem {
@@ -25,6 +36,10 @@ struct GemmProblem {
     float *y;
     int64_t ldy;
     const int32_t *offsets;  // grouped only: [experts+1] on the device
+    // grouped only, optional: sorted row r reads activation row row_ids[r]
+    // (clamped to [0, src_rows)) instead of row r
+    const int32_t *row_ids;
+    int64_t src_rows;
     // block sums
     int32_t *sums;
     int64_t m0, m1, n0, n1, expert;

@@ -200,7 +200,82 @@ __global__ __launch_bounds__(kThreads) void quantize_h32_kernel(
     }
 }
 
+// ---- SwiGLU feeding the down projection of an expert layer.  The pages say
+// only that the route covers the expert matmuls ("Where the engine is going:
+// HRX and the NPU", section "4-bit activations reach the MoE experts"); the
+// down projection's input h = silu(gate) * up is rotated and quantized like
+// any activation, in the same kernel.
+
+// e^x in fp32, every step one correctly rounded fp32 operation (the file is
+// compiled without contraction): Cody-Waite range reduction n = rint(x log2 e),
+// r = (x - n ln2_hi) - n ln2_lo (ln2_hi has 16 significant bits, so n ln2_hi
+// is exact), the degree-6 Taylor polynomial of e^r in Horner form, then a
+// scaling by 2^n.  x is clamped to [-87, 88].
+__device__ __forceinline__ float exp_f32(float x)
+{
+    x = fminf(fmaxf(x, -87.0f), 88.0f);
+    const float log2e = (float)1.4426950408889634;
+    const float ln2_hi = 0.693145751953125f;
+    const float ln2_lo = (float)(0.6931471805599453 - 0.693145751953125);
+    const float n = rintf(x * log2e);
+    const float r = (x - n * ln2_hi) - n * ln2_lo;
+    float p = 1.0f / 720.0f;
+    p = p * r + 1.0f / 120.0f;
+    p = p * r + 1.0f / 24.0f;
+    p = p * r + 1.0f / 6.0f;
+    p = p * r + 0.5f;
+    p = p * r + 1.0f;
+    p = p * r + 1.0f;
+    return ldexpf(p, (int)n);
+}
+
+// silu(g) = g / (1 + e^-g), IEEE division
+__device__ __forceinline__ float silu_f32(float g)
+{
+    const float den = 1.0f + exp_f32(-g);
+    return g / den;
+}
+
+// One quad of lanes per 32-block of h, grid-stride; all four lanes of a quad
+// walk the same blocks (the DPP exchanges stay inside the quad).
+template <int BITS>
+__global__ __launch_bounds__(kThreads) void swiglu_quantize_kernel(
+    const float *__restrict__ gu, int64_t inter, int64_t ldgu, int64_t nblk_total,
+    uint8_t *__restrict__ codes, float *__restrict__ scales)
+{
+    const int t = threadIdx.x & 3;
+    const int64_t nb = inter / 32;
+    const int64_t stride = (int64_t)gridDim.x * (kThreads / 4);
+    for (int64_t blk = (int64_t)blockIdx.x * (kThreads / 4) + (threadIdx.x >> 2); blk < nblk_total;
+         blk += stride) {
+        const int64_t row = blk / nb, b = blk - row * nb;
+        float g[8], u[8], v[8];
+        load8(gu + row * ldgu + b * 32, t, g);
+        load8(gu + row * ldgu + inter + b * 32, t, u);
+#pragma unroll
+        for (int i = 0; i < 8; i++)
+            v[i] = silu_f32(g[i]) * u[i];
+        quantize_block<BITS>(v, t, 1, row, b, inter, nb, codes, scales);
+    }
+}
+
 } // namespace
+
+hipError_t launch_swiglu_quantize(const float *gu, int64_t rows, int64_t inter, int64_t ldgu,
+                                  int act_bits, void *codes, float *scales, hipStream_t stream)
+{
+    const int64_t nblk = rows * (inter / 32);
+    if (nblk == 0)
+        return hipSuccess;
+    const int64_t needed = (nblk + kThreads / 4 - 1) / (kThreads / 4);
+    const dim3 grid((unsigned)(needed < 2048 ? needed : 2048));
+    uint8_t *c = static_cast<uint8_t *>(codes);
+    if (act_bits == 4)
+        swiglu_quantize_kernel<4><<<grid, kThreads, 0, stream>>>(gu, inter, ldgu, nblk, c, scales);
+    else
+        swiglu_quantize_kernel<8><<<grid, kThreads, 0, stream>>>(gu, inter, ldgu, nblk, c, scales);
+    return hipGetLastError();
+}
 
 hipError_t launch_quantize(const void *x, int dtype, int64_t m, int64_t k, int64_t ldx,
                            int act_bits, int rotate, void *codes, float *scales,

@@ -91,6 +91,17 @@ def draw_routing(rng, tokens, experts, topk):
     return tok.astype(np.int64), exp.astype(np.int64), offsets
 
 
+def draw_routes(rng, tokens, experts, topk):
+    """Routed choices in entry order (entry t*topk + j): expert ids int32
+    [tokens*topk], topk distinct experts per token, and routing weights fp32
+    (a softmax over topk standard-normal logits per token)."""
+    choice = np.argsort(rng.random((tokens, experts)), axis=1)[:, :topk]
+    logits = rng.standard_normal((tokens, topk))
+    w = np.exp(logits - logits.max(axis=1, keepdims=True))
+    w /= w.sum(axis=1, keepdims=True)
+    return choice.reshape(-1).astype(np.int32), w.reshape(-1).astype(np.float32)
+
+
 # name -> recipe.  'gemms' lists (input name, weight name) pairs in step order.
 CONFIGS = {
     "tiny": dict(desc="Tiny W4A4: M=16, K=256, N=128, fp32 activations",

@@ -234,6 +234,76 @@ bpg_status w4a4_grouped_gemm(const void *codes, const float *scales, int act_bit
                              int64_t ldy, void *stream);
 
 /*
+ * The expert layer around the grouped product ("Where the engine is going: HRX
+ * and the NPU", section "4-bit activations reach the MoE experts": the route
+ * covers the expert matmuls; the pages give no detail of the layer around
+ * them, so the steps below are this library's reading).  A layer of T tokens,
+ * each routed to topk experts (entry t*topk + j), runs as
+ *   moe_route_sort -> quantize_act_h32 (T token rows, once)
+ *   -> w4a4_grouped_gemm_gather (gate and up projections, rows gathered by
+ *      token) -> swiglu_quantize_h32 -> w4a4_grouped_gemm (down projection)
+ *   -> moe_combine.
+ *
+ * moe_route_sort: sorts the entries by expert, stably (entry order inside an
+ * expert), on the GPU, in one workgroup.
+ *   expert_of_dev   device, int32 [tokens*topk]; ids outside [0, experts) are
+ *                   clamped (unspecified grouping, in-bounds accesses)
+ *   offsets_dev     device, int32 [experts+1]: expert e owns sorted rows
+ *                   [offsets[e], offsets[e+1])
+ *   row_token_dev   device, int32 [tokens*topk]: the token of each sorted row
+ *   slot_of_dev     device, int32 [tokens*topk]: the sorted row of each entry
+ * Limits: experts <= 512, tokens*topk <= 2^24.  Pointers 4-byte aligned.
+ * Errors: NULL, SHAPE, ALIGN, DEVICE, LAUNCH.
+ */
+bpg_status moe_route_sort(const int32_t *expert_of_dev, int64_t tokens, int64_t topk,
+                          int64_t experts, int32_t *offsets_dev, int32_t *row_token_dev,
+                          int32_t *slot_of_dev, void *stream);
+
+/*
+ * w4a4_grouped_gemm_gather: as w4a4_grouped_gemm, but sorted row r reads
+ * activation row row_ids_dev[r] (clamped to [0, src_rows)) of codes and
+ * scales, which hold src_rows rows (e.g. the tokens, quantized once); y has
+ * total_rows rows in sorted order.  src_rows * (bytes per code row) < 2^31.
+ * row_ids_dev is device int32 [total_rows], 4-byte aligned.
+ * Errors: NULL, SHAPE, ALIGN, DTYPE, STAMP, DEVICE, LAUNCH.
+ */
+bpg_status w4a4_grouped_gemm_gather(const void *codes, const float *scales, int act_bits,
+                                    int64_t src_rows, const int32_t *row_ids_dev,
+                                    int64_t total_rows, const int32_t *expert_offsets_dev,
+                                    const bpg_weights_desc *w, const void *w_dev, float *y,
+                                    int64_t ldy, void *stream);
+
+/*
+ * swiglu_quantize_h32: the down projection's input.  gu is device fp32
+ * [rows][ldgu] with the gate projection in columns [0, inter) and the up
+ * projection in [inter, 2*inter) (ldgu >= 2*inter, ldgu % 4 == 0).
+ * h = silu(gate) * up in fp32, with silu(g) = g / (1 + e^-g) (IEEE division)
+ * and e^x computed in fp32 as: x clamped to [-87, 88]; n = rint(x * fp32(log2 e));
+ * r = (x - n * 0.693145751953125) - n * fp32(ln 2 - 0.693145751953125);
+ * p = Horner form of the degree-6 Taylor polynomial of e^r with coefficients
+ * fp32(1/720), fp32(1/120), fp32(1/24), fp32(1/6), 0.5, 1, 1; e^x = p * 2^n;
+ * every step one fp32 operation, no FMA.  Then h is rotated and quantized
+ * exactly as quantize_act_h32 does (codes [rows][inter/2] or [rows][inter],
+ * scales [rows][inter/32]).
+ * Errors: NULL, SHAPE, ALIGN, DTYPE, DEVICE, LAUNCH.
+ */
+bpg_status swiglu_quantize_h32(const float *gu, int64_t rows, int64_t inter, int64_t ldgu,
+                               int act_bits, void *codes, float *scales, void *stream);
+
+/*
+ * moe_combine: y[t][c] = sum over j = 0..topk-1, in that order, of
+ * weights[t*topk + j] * dn[slot_of[t*topk + j]][c]; the accumulator starts at
+ * 0 and every step is one fp32 fma.  dn is device fp32 [rows][lddn] (sorted
+ * rows; slot values are clamped to [0, rows)); y is device fp32
+ * [tokens][ldy], overwritten.  hidden % 4 == 0, lddn and ldy >= hidden and
+ * multiples of 4; dn and y 16-byte aligned, slot_of and weights 4-byte.
+ * Errors: NULL, SHAPE, ALIGN, DEVICE, LAUNCH.
+ */
+bpg_status moe_combine(const float *dn, int64_t lddn, int64_t rows, const int32_t *slot_of_dev,
+                       const float *weights_dev, int64_t tokens, int64_t topk, int64_t hidden,
+                       float *y, int64_t ldy, void *stream);
+
+/*
  * Parity and debug: the exact int32 block dot products
  * S[m][n][b] = sum_i q_a[m][32b+i] * (u[n][32b+i] - 8), computed by the same
  * matrix-instruction main loop as w4a4_gemm, for rows [m0, m1) and columns

@@ -239,3 +239,64 @@ def test_unrotated_pack_errors_and_stamp():
 def test_unrotated_valid_calls_stop_at_device_check_without_gpu():
     assert q_u() == DEVICE
     assert gemm_u() == DEVICE
+
+
+# ------------------------------------------------------------ expert layer glue
+
+def test_route_sort_errors():
+    lib = bb.lib()
+    f = lambda **kw: lib.moe_route_sort(kw.get("e", P), kw.get("t", 4), kw.get("k", 2),
+                                        kw.get("E", 8), kw.get("off", P2), kw.get("rt", P),
+                                        kw.get("so", P2), NUL)
+    assert f(E=0) == SHAPE and f(E=513) == SHAPE and f(k=0) == SHAPE and f(t=-1) == SHAPE
+    assert f(t=1 << 24, k=2) == SHAPE
+    assert f(off=NUL) == NULL and f(e=NUL) == NULL and f(rt=NUL) == NULL
+    assert f(so=ctypes.c_void_p(0x200002)) == ALIGN
+    if not os.path.exists("/dev/kfd"):
+        assert f() == DEVICE
+        assert f(t=0, e=NUL, rt=NUL, so=NUL) == DEVICE
+
+
+def test_gather_errors():
+    lib = bb.lib()
+    d = good_desc(e=3)
+    f = lambda **kw: lib.w4a4_grouped_gemm_gather(
+        kw.get("codes", P), kw.get("scales", P2), kw.get("bits", 4), kw.get("src", 10),
+        kw.get("ids", P), kw.get("rows", 4), kw.get("off", P), ctypes.byref(kw.get("desc", d)),
+        kw.get("wdev", P), kw.get("y", P2), kw.get("ldy", 64), NUL)
+    assert f(ids=NUL) == NULL
+    assert f(src=0) == SHAPE and f(src=-1) == SHAPE and f(rows=-2) == SHAPE
+    assert f(src=1 << 30) == SHAPE           # gathered rows need 32-bit offsets
+    assert f(ids=ctypes.c_void_p(0x100002)) == ALIGN
+    assert f(bits=5) == DTYPE and f(desc=_desc_with(magic=2)) == STAMP
+    if not os.path.exists("/dev/kfd"):
+        assert f() == DEVICE
+
+
+def test_swiglu_quantize_errors():
+    lib = bb.lib()
+    f = lambda **kw: lib.swiglu_quantize_h32(kw.get("gu", P), kw.get("rows", 4),
+                                             kw.get("inter", 64), kw.get("ld", 128),
+                                             kw.get("bits", 4), kw.get("codes", P2),
+                                             kw.get("scales", P), NUL)
+    assert f(bits=3) == DTYPE
+    assert f(inter=48) == SHAPE and f(ld=127) == SHAPE and f(rows=-1) == SHAPE
+    assert f(gu=NUL) == NULL and f(codes=NUL) == NULL
+    assert f(gu=MIS) == ALIGN and f(ld=130) == ALIGN
+    if not os.path.exists("/dev/kfd"):
+        assert f() == DEVICE
+        assert f(rows=0, gu=NUL, codes=NUL, scales=NUL) == DEVICE
+
+
+def test_combine_errors():
+    lib = bb.lib()
+    f = lambda **kw: lib.moe_combine(kw.get("dn", P), kw.get("lddn", 64), kw.get("rows", 8),
+                                     kw.get("slot", P2), kw.get("w", P), kw.get("t", 4),
+                                     kw.get("k", 2), kw.get("h", 64), kw.get("y", P2),
+                                     kw.get("ldy", 64), NUL)
+    assert f(h=62) == SHAPE and f(lddn=32) == SHAPE and f(ldy=32) == SHAPE and f(k=0) == SHAPE
+    assert f(rows=0) == SHAPE
+    assert f(dn=NUL) == NULL and f(slot=NUL) == NULL and f(w=NUL) == NULL and f(y=NUL) == NULL
+    assert f(dn=MIS) == ALIGN and f(lddn=66) == ALIGN and f(w=ctypes.c_void_p(0x100002)) == ALIGN
+    if not os.path.exists("/dev/kfd"):
+        assert f() == DEVICE
