@@ -13,17 +13,19 @@ last-level cache cannot hold them.
 Other workloads (--workload): the long-prompt and FFN-sized GEMM, three
 weight-streaming cases with 16 tokens, and the two grouped expert GEMMs of the
 MoE workload (512 tokens routed top-8 over 128 experts; `value` counts the 512
-tokens).
+tokens), and the whole expert layer (moe512_layer: expert sort, token
+quantization, gathered gate/up GEMM, SwiGLU-rotate-quantize, down GEMM,
+weighted combine; `kernel_us` gives each kernel's own duration).
 
 Prints ONE JSON line.  `value` is prompt tokens per second of the step.  The
 `roofline` object covers the GEMM kernel (the dominant kernel).  Its average
 duration is measured with HIP events recorded on the launch stream around
-every GEMM in the timed region.  With many rows the kernel is bound by its
-fp32 VALU epilogue (two FMAs per output element and 32-block), so the
-roofline is taken against the fp32 vector peak; the int8 matrix-core view
-(effective TOPS against the dense int8 peak) is reported beside it.  With 32
-rows or fewer it is bound by the weight stream: the roofline is HBM bytes per
-second against the HBM peak.
+every GEMM in the timed region.  The bound is whichever algorithmic floor is
+larger: the fp32 VALU epilogue (two FMAs per output element and 32-block)
+against the fp32 vector peak (dense shapes with many rows), or the HBM bytes
+against the HBM peak (a few rows, and the grouped expert GEMMs, whose weight
+stream is larger); the int8 matrix-core view (effective TOPS against the
+dense int8 peak) is reported beside it.
 `traffic` comes from the committed rocprofv3 counter summary for this kernel
 and workload, and is null if the kernel source changed since it was taken.
 `cpu_baseline` times the CPU oracle on the same workload (test
@@ -68,6 +70,9 @@ WORKLOADS = {
                       w="w_gu"),
     "moe512_dn": dict(m=4096, k=768, n=2048, experts=128, tokens=512, src="moe512", x="x_dn",
                       w="w_dn"),
+    # the whole expert layer: expert sort, token quantization, gathered gate/up
+    # GEMM, SwiGLU-rotate-quantize, down GEMM, weighted combine
+    "moe512_layer": dict(m=512, k=2048, n=2048, experts=128, tokens=512, layer=True),
 }
 # kernel sources of the GEMM paths (the tiled and grouped kernels, and the
 # weight-stream kernel used for a few rows)
@@ -144,6 +149,21 @@ def cpu_baseline(data, wl, name, bits, seconds):
                       "output), %d repetition(s) in %.1f s" % (name, m, k, m, k, n, reps, el)}
 
 
+def roofline_of(kernel, m, k, n, bits, experts, seconds, traffic):
+    """The binding roofline of one GEMM launch: whichever algorithmic floor is
+    larger, the HBM bytes at 8 TB/s or the fp32 epilogue (two FMAs per output
+    and block) at the fp32 vector peak."""
+    gbytes = gemm_bytes(m, k, n, bits, experts)
+    epi_flops = 4.0 * m * n * (k // 32)
+    if gbytes / PEAK_HBM >= epi_flops / PEAK_FP32_FLOPS:
+        return {"bound": "hbm", "achieved": gbytes / seconds / 1e9, "peak": PEAK_HBM / 1e9,
+                "unit": "GB/s", "frac": gbytes / seconds / PEAK_HBM, "traffic": traffic,
+                "kernel": kernel}
+    return {"bound": "alu", "achieved": epi_flops / seconds / 1e12,
+            "peak": PEAK_FP32_FLOPS / 1e12, "unit": "TFLOP/s",
+            "frac": epi_flops / seconds / PEAK_FP32_FLOPS, "traffic": traffic, "kernel": kernel}
+
+
 def copy_calibration(nbytes):
     import torch
     n = int(nbytes) // 4
@@ -174,6 +194,8 @@ def main():
         return
     bb.lib()
     wl = WORKLOADS[args.workload]
+    if wl.get("layer"):
+        return main_layer(args, wl)
     m, k, n, bits = wl["m"], wl["k"], wl["n"], args.bits
     experts = wl.get("experts", 1)
     data = synth.make(wl.get("src", args.workload))
@@ -237,22 +259,11 @@ def main():
     gemm_s = gemm_ms * 1e-3
     ops = 2.0 * m * n * k
     eff_tops = ops / gemm_s / 1e12
-    epi_flops = 4.0 * m * n * (k // 32)   # algorithmic: two fp32 FMAs per output and block
     gbytes = gemm_bytes(m, k, n, bits, experts)
     traffic = measured_traffic(args.workload, bits)
 
     kernel = "w4a4_gemm" if experts == 1 else "w4a4_grouped_gemm"
-    if experts == 1 and m <= 32:
-        # a few rows: the weight stream from HBM binds
-        roofline = {"bound": "hbm", "achieved": gbytes / gemm_s / 1e9, "peak": PEAK_HBM / 1e9,
-                    "unit": "GB/s", "frac": gbytes / gemm_s / PEAK_HBM, "traffic": traffic,
-                    "kernel": kernel}
-    else:
-        # the fp32 epilogue (two VALU operations per output and block) binds
-        roofline = {"bound": "alu", "achieved": epi_flops / gemm_s / 1e12,
-                    "peak": PEAK_FP32_FLOPS / 1e12, "unit": "TFLOP/s",
-                    "frac": epi_flops / gemm_s / PEAK_FP32_FLOPS, "traffic": traffic,
-                    "kernel": kernel}
+    roofline = roofline_of(kernel, m, k, n, bits, experts, gemm_s, traffic)
 
     out = {
         "metric": "prompt tokens/s + effective TOPS (% int8 MFMA peak) for rotated W4A4 GEMM, M=512",
@@ -289,6 +300,163 @@ def main():
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(data, wl, args.workload, bits, args.cpu_seconds)
     print(json.dumps(out))
+
+
+def main_layer(args, wl):
+    """One step = one expert layer over 512 tokens (moe512: hidden 2048, 128
+    experts, top-8, expert intermediate 768)."""
+    import torch
+
+    from bit_prefill_gemm_amd import binding as bb
+    from bit_prefill_gemm_amd import synth
+
+    bits = args.bits
+    data = synth.make("moe512")
+    c = data["cfg"]
+    T, H, E, K8, I = c["tokens"], c["hidden"], c["experts"], c["topk"], c["inter"]
+    rows = T * K8
+    e_np, w_np = synth.draw_routes(np.random.default_rng(21), T, E, K8)
+    dev = torch.device("cuda:0")
+    Wgu0 = bb.rotate_pack_weights(data["w_gu"], bb.SRC_Q4_0_ROTATED, 2 * I, H, E)
+    Wdn0 = bb.rotate_pack_weights(data["w_dn"], bb.SRC_Q4_0_ROTATED, H, I, E)
+    gu_img = torch.from_numpy(Wgu0.image).to(dev)
+    dn_img = torch.from_numpy(Wdn0.image).to(dev)
+    x0 = torch.from_numpy(data["x_tokens"].view(np.int16)).to(dev).view(torch.bfloat16)
+    per_copy = gu_img.numel() + dn_img.numel() + x0.numel() * 2
+    copies = max(1, int(math.ceil(args.cold_bytes / per_copy)))
+    Wgu = [bb.Weights(Wgu0.desc, gu_img if j == 0 else gu_img.clone()) for j in range(copies)]
+    Wdn = [bb.Weights(Wdn0.desc, dn_img if j == 0 else dn_img.clone()) for j in range(copies)]
+    xs = [x0 if j == 0 else x0.clone() for j in range(copies)]
+    expert_of = torch.from_numpy(e_np).to(dev)
+    weights = torch.from_numpy(w_np).to(dev)
+    ab = 2 if bits == 4 else 1
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    row_token = torch.empty(rows, dtype=torch.int32, device=dev)
+    slot_of = torch.empty(rows, dtype=torch.int32, device=dev)
+    codes = torch.empty((T, H // ab), dtype=torch.uint8, device=dev)
+    scales = torch.empty((T, H // 32), dtype=torch.float32, device=dev)
+    gu = torch.empty((rows, 2 * I), dtype=torch.float32, device=dev)
+    hc = torch.empty((rows, I // ab), dtype=torch.uint8, device=dev)
+    hs = torch.empty((rows, I // 32), dtype=torch.float32, device=dev)
+    dn = torch.empty((rows, H), dtype=torch.float32, device=dev)
+    y = torch.empty((T, H), dtype=torch.float32, device=dev)
+    stream = torch.cuda.Stream(device=dev)
+    lib = bb.lib()
+    sh = bb._stream_handle(stream)
+
+    def check(st, what):
+        if st != 0:
+            raise bb.BpgError(st, what)
+
+    kernels = {
+        "moe_route_sort": lambda j: check(lib.moe_route_sort(
+            bb._dptr(expert_of), T, K8, E, bb._dptr(offsets), bb._dptr(row_token),
+            bb._dptr(slot_of), sh), "sort"),
+        "quantize_act_h32": lambda j: bb.quantize_act_h32(xs[j], bits, codes=codes, scales=scales,
+                                                          stream=stream),
+        "w4a4_grouped_gemm_gather": lambda j: bb.w4a4_grouped_gemm_gather(
+            codes, scales, bits, row_token, offsets, Wgu[j], y=gu, stream=stream),
+        "swiglu_quantize_h32": lambda j: bb.swiglu_quantize_h32(gu, I, bits, codes=hc, scales=hs,
+                                                                stream=stream),
+        "w4a4_grouped_gemm": lambda j: bb.w4a4_grouped_gemm(hc, hs, bits, offsets, Wdn[j], y=dn,
+                                                            stream=stream),
+        "moe_combine": lambda j: bb.moe_combine(dn, slot_of, weights, T, K8, y=y, stream=stream),
+    }
+
+    def step(j):
+        for f in kernels.values():
+            f(j)
+
+    with torch.cuda.stream(stream):
+        for i in range(args.warmup):
+            step(i % copies)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step((args.warmup + i) % copies)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        # each kernel's own duration: event pairs around it alone, in step order
+        reps = min(args.steps, 30)
+        evs = {name: [] for name in kernels}
+        for i in range(reps):
+            j = i % copies
+            for name, f in kernels.items():
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                f(j)
+                e1.record(stream)
+                evs[name].append((e0, e1))
+        torch.cuda.synchronize()
+    kernel_us = {name: 1e3 * float(np.mean([a.elapsed_time(b) for a, b in v]))
+                 for name, v in evs.items()}
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    gate_s = kernel_us["w4a4_grouped_gemm_gather"] * 1e-6
+    roofline = roofline_of("w4a4_grouped_gemm_gather", rows, H, 2 * I, bits, E, gate_s, None)
+    out = {
+        "metric": "prompt tokens/s + effective TOPS (% int8 MFMA peak) for rotated W4A4 GEMM, M=512",
+        "value": T / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i8" if bits == 8 else "i4",
+        "data": "synthetic",
+        "config": {"workload": "moe512_layer: expert layer over %d tokens, hidden %d, %d experts, "
+                               "top-%d, expert intermediate %d, bf16 activations, rotated Q4_0 "
+                               "weights, %d-bit activation codes" % (T, H, E, K8, I, bits),
+                   "tokens": T, "hidden": H, "experts": E, "topk": K8, "inter": I,
+                   "act_bits": bits, "cold_copies": copies},
+        "roofline": roofline,
+        "kernel_us": kernel_us,
+        "step_us": ms_per_step * 1e3,
+        "gemm_source_sha256_16": source_hash(),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_layer(data, e_np, w_np, bits, args.cpu_seconds)
+    print(json.dumps(out))
+
+
+def cpu_baseline_layer(data, e_np, w_np, bits, seconds):
+    """The oracle's expert layer (same steps, fp64 GEMM outputs rounded to fp32
+    between steps) on the same 512 tokens."""
+    import oracle
+    c = data["cfg"]
+    T, H, E, K8, I = c["tokens"], c["hidden"], c["experts"], c["topk"], c["inter"]
+    gu_dec = [oracle.q4_0_decode(data["w_gu"][e], H) for e in range(E)]
+    dn_dec = [oracle.q4_0_decode(data["w_dn"][e], I) for e in range(E)]
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        off, entry, slot = oracle.route_sort(e_np, E)
+        q, d, _ = oracle.quantize(data["x_tokens"], bits)
+        rt = entry // K8
+        qg, dg = q[rt], d[rt]
+        gu = np.zeros((T * K8, 2 * I), dtype=np.float32)
+        for e in range(E):
+            a, b = off[e], off[e + 1]
+            if b > a:
+                w, dw = gu_dec[e]
+                gu[a:b] = oracle.gemm_rect(qg[a:b], dg[a:b], w, dw, 0, b - a, 0, 2 * I)
+        hq, hd, _ = oracle.swiglu_quantize(gu, I, bits)
+        dn = np.zeros((T * K8, H), dtype=np.float32)
+        for e in range(E):
+            a, b = off[e], off[e + 1]
+            if b > a:
+                w, dw = dn_dec[e]
+                dn[a:b] = oracle.gemm_rect(hq[a:b], hd[a:b], w, dw, 0, b - a, 0, H)
+        oracle.moe_combine(dn, slot, w_np, T, K8)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or reps >= 20:
+            break
+    return {"value": reps * T / el, "unit": "tokens/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": "whole moe512 expert layer (sort, quantize, gate/up, SwiGLU-quantize, "
+                      "down, combine), %d repetition(s) in %.1f s" % (reps, el)}
 
 
 if __name__ == "__main__":

@@ -74,7 +74,7 @@ __global__ __launch_bounds__(kSortThreads) void route_sort_kernel(
         int rank = 0;
         while (left != 0) { // uniform: every lane sees the same mask
             const int leader = __builtin_ctzll(left);
-            const int x = __shfl(e, leader);
+            const int x = __builtin_amdgcn_readlane(e, leader);
             const uint64_t same = __ballot(valid && e == x) & left;
             if (valid && e == x) {
                 rank = __builtin_popcountll(same & ((1ull << lane) - 1ull));
