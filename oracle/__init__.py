@@ -66,6 +66,11 @@ def _load():
         "orc_ref_points": (None, [_p, ctypes.c_int, _i64, _p, _p, _i64, _p, _p, _i64, _p]),
         "orc_num_threads": (ctypes.c_int, []),
         "orc_exp_f32": (ctypes.c_float, [ctypes.c_float]),
+        "orc_rotate_n_f32": (None, [_p, _p, _i64, ctypes.c_int]),
+        "orc_rotate_n_f64": (None, [_p, _p, _i64, ctypes.c_int]),
+        "orc_quantize_rot": (_i64, [_p, ctypes.c_int, _i64, _i64, _i64, ctypes.c_int, ctypes.c_int,
+                                    _p, _p]),
+        "orc_quantize_weights_q4_0_rot": (None, [_p, ctypes.c_int, _i64, _i64, ctypes.c_int, _p]),
         "orc_silu_f32": (ctypes.c_float, [ctypes.c_float]),
         "orc_swiglu_quantize": (_i64, [_p, _i64, _i64, _i64, ctypes.c_int, _p, _p]),
         "orc_moe_combine": (None, [_p, _i64, _p, _p, _i64, _i64, _i64, _p, _i64]),
@@ -300,4 +305,46 @@ def moe_combine(dn: np.ndarray, slot_of: np.ndarray, weights: np.ndarray, tokens
     out = np.empty((tokens, hidden), dtype=np.float32)
     _load().orc_moe_combine(_ptr(dn), dn.shape[1], _ptr(slot), _ptr(w), tokens, topk, hidden,
                             _ptr(out), hidden)
+    return out
+
+
+# ---------------------------------------------------------------- longer rotations
+
+def rotate_n_f32(x: np.ndarray, n: int) -> np.ndarray:
+    """H_n (Sylvester order) over each trailing span of n values, fp32, times fp32(1/sqrt n)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    assert n in (32, 64, 128) and x.shape[-1] % n == 0
+    v = np.empty_like(x)
+    _load().orc_rotate_n_f32(_ptr(x), _ptr(v), x.size // n, n)
+    return v
+
+
+def rotate_n_f64(x: np.ndarray, n: int) -> np.ndarray:
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    assert n in (32, 64, 128) and x.shape[-1] % n == 0
+    v = np.empty_like(x)
+    _load().orc_rotate_n_f64(_ptr(x), _ptr(v), x.size // n, n)
+    return v
+
+
+def quantize_rot(x: np.ndarray, rot: int, bits: int = 4):
+    """Activation codes with rotation rot (0 = none, 32, 64, 128); as quantize()."""
+    assert bits in (4, 8) and rot in (0, 32, 64, 128)
+    x, dt = _act(x)
+    m, k = x.shape
+    assert k % max(rot, 32) == 0
+    q = np.empty((m, k), dtype=np.int8)
+    d = np.empty((m, k // 32), dtype=np.float32)
+    ties = _load().orc_quantize_rot(_ptr(x), dt, m, k, k, bits, rot, _ptr(q), _ptr(d))
+    return q, d, int(ties)
+
+
+def quantize_weights_q4_0_rot(w: np.ndarray, rot: int) -> np.ndarray:
+    """Float weights [n, k] -> canonical Q4_0 blocks [n, k/32, 18] with rotation rot."""
+    assert rot in (0, 32, 64, 128)
+    w, dt = _act(w)
+    n, k = w.shape
+    assert k % max(rot, 32) == 0
+    out = np.empty((n, k // 32, 18), dtype=np.uint8)
+    _load().orc_quantize_weights_q4_0_rot(_ptr(w), dt, n, k, rot, _ptr(out))
     return out

@@ -282,6 +282,30 @@ void orc_q4_0_decode(const uint8_t *blocks, int64_t rows, int64_t k, int8_t *w, 
  * w: [n][k] fp32 (dtype 0) or bf16 bits (dtype 1).  rotate = 0 quantizes
  * without the transform.  blocks: [n][k/32] x 18 bytes.
  */
+/* Q4_0 block of 32 (already rotated) fp64 values. */
+static void q4_0_block(const double v[QK], uint8_t blk[18])
+{
+    double amax = 0.0;
+    for (int i = 0; i < QK; i++)
+        if (fabs(v[i]) > amax)
+            amax = fabs(v[i]);
+    uint16_t hbits = orc_f64_to_f16(amax / 7.0);
+    double dwv = orc_f16_to_f64(hbits);
+    blk[0] = (uint8_t)(hbits & 0xff);
+    blk[1] = (uint8_t)(hbits >> 8);
+    int u[QK];
+    for (int i = 0; i < QK; i++) {
+        double kq = dwv == 0.0 ? 0.0 : rint(v[i] / dwv);
+        if (kq < -8.0)
+            kq = -8.0;
+        if (kq > 7.0)
+            kq = 7.0;
+        u[i] = (int)kq + 8;
+    }
+    for (int j = 0; j < 16; j++)
+        blk[2 + j] = (uint8_t)(u[j] | (u[j + 16] << 4));
+}
+
 void orc_quantize_weights_q4_0(const void *w, int dtype, int64_t n, int64_t k, int rotate,
                                uint8_t *blocks)
 {
@@ -295,26 +319,122 @@ void orc_quantize_weights_q4_0(const void *w, int dtype, int64_t n, int64_t k, i
                 orc_rotate_f64(in, v, 1);
             else
                 memcpy(v, in, sizeof v);
-            double amax = 0.0;
-            for (int i = 0; i < QK; i++)
-                if (fabs(v[i]) > amax)
-                    amax = fabs(v[i]);
-            uint16_t hbits = orc_f64_to_f16(amax / 7.0);
-            double dwv = orc_f16_to_f64(hbits);
-            uint8_t *blk = blocks + (r * nb + b) * 18;
-            blk[0] = (uint8_t)(hbits & 0xff);
-            blk[1] = (uint8_t)(hbits >> 8);
-            int u[QK];
-            for (int i = 0; i < QK; i++) {
-                double kq = dwv == 0.0 ? 0.0 : rint(v[i] / dwv);
-                if (kq < -8.0)
-                    kq = -8.0;
-                if (kq > 7.0)
-                    kq = 7.0;
-                u[i] = (int)kq + 8;
+            q4_0_block(v, blocks + (r * nb + b) * 18);
+        }
+}
+
+/* ------------------------------------------------------------------ */
+/* Rotations longer than 32 [27B "What's next": rotations larger than   */
+/* 32 spread outliers further].  Reading: the Sylvester-order H_n over  */
+/* each span of n = 64 or 128 consecutive values (n = 32 is the route's */
+/* rotation), butterflies h = 1 .. n/2 in the stage order and sign      */
+/* convention of the 32-point one, then times fp32(1/sqrt n); the       */
+/* 32-value quantization blocks and their scales are unchanged.         */
+/* ------------------------------------------------------------------ */
+
+#define MAXROT 128
+
+/* 1/sqrt(n) for n = 32, 64, 128: sqrt(2)/8, 1/8, sqrt(2)/16 (the divisions
+   by powers of two are exact). */
+static double inv_sqrt_n_f64(int n)
+{
+    return n == 64 ? 0.125 : (n == 128 ? sqrt(2.0) / 16.0 : sqrt(2.0) / 8.0);
+}
+
+static void wht_butterflies_f32(float *v, int n)
+{
+    for (int h = 1; h < n; h <<= 1)
+        for (int j = 0; j < n; j++)
+            if ((j & h) == 0) {
+                float a = v[j], b = v[j + h];
+                v[j] = a + b;
+                v[j + h] = a - b;
             }
-            for (int j = 0; j < 16; j++)
-                blk[2 + j] = (uint8_t)(u[j] | (u[j + 16] << 4));
+}
+
+static void wht_butterflies_f64(double *v, int n)
+{
+    for (int h = 1; h < n; h <<= 1)
+        for (int j = 0; j < n; j++)
+            if ((j & h) == 0) {
+                double a = v[j], b = v[j + h];
+                v[j] = a + b;
+                v[j + h] = a - b;
+            }
+}
+
+/* v = fp32(H_n x) * fp32(1/sqrt n) for nspan spans of n values. */
+void orc_rotate_n_f32(const float *x, float *v, int64_t nspan, int n)
+{
+    const float c = (float)inv_sqrt_n_f64(n);
+    for (int64_t t = 0; t < nspan; t++) {
+        float w[MAXROT];
+        memcpy(w, x + t * n, sizeof(float) * n);
+        wht_butterflies_f32(w, n);
+        for (int i = 0; i < n; i++)
+            v[t * n + i] = w[i] * c;
+    }
+}
+
+void orc_rotate_n_f64(const double *x, double *v, int64_t nspan, int n)
+{
+    const double c = inv_sqrt_n_f64(n);
+    for (int64_t t = 0; t < nspan; t++) {
+        double w[MAXROT];
+        memcpy(w, x + t * n, sizeof(double) * n);
+        wht_butterflies_f64(w, n);
+        for (int i = 0; i < n; i++)
+            v[t * n + i] = w[i] * c;
+    }
+}
+
+/*
+ * Activation codes with rotation rot (0: none, or 32, 64, 128; k a multiple
+ * of rot): every span of rot values is rotated in fp32, then every 32-block
+ * is quantized as orc_quantize does.  Returns the number of .5 quotients.
+ */
+int64_t orc_quantize_rot(const void *x, int dtype, int64_t m, int64_t k, int64_t ldx, int bits,
+                         int rot, int8_t *q, float *d)
+{
+    const int span = rot == 0 ? QK : rot;
+    const int64_t nb = k / QK, ns = k / span;
+    int64_t ties = 0;
+#pragma omp parallel for reduction(+ : ties) schedule(static)
+    for (int64_t r = 0; r < m; r++) {
+        for (int64_t s = 0; s < ns; s++) {
+            float xin[MAXROT], v[MAXROT];
+            for (int i = 0; i < span; i++)
+                xin[i] = load_act(x, dtype, r * ldx + s * span + i);
+            if (rot)
+                orc_rotate_n_f32(xin, v, 1, span);
+            else
+                memcpy(v, xin, sizeof(float) * span);
+            for (int b = 0; b < span / QK; b++) {
+                const int64_t blk = s * (span / QK) + b;
+                ties += quantize_block(v + b * QK, bits, q + r * k + blk * QK, d + r * nb + blk);
+            }
+        }
+    }
+    return ties;
+}
+
+/* Q4_0 weights with rotation rot (0, 32, 64 or 128), rotated in fp64. */
+void orc_quantize_weights_q4_0_rot(const void *w, int dtype, int64_t n, int64_t k, int rot,
+                                   uint8_t *blocks)
+{
+    const int span = rot == 0 ? QK : rot;
+    const int64_t nb = k / QK, ns = k / span;
+    for (int64_t r = 0; r < n; r++)
+        for (int64_t s = 0; s < ns; s++) {
+            double in[MAXROT], v[MAXROT];
+            for (int i = 0; i < span; i++)
+                in[i] = (double)load_act(w, dtype, r * k + s * span + i);
+            if (rot)
+                orc_rotate_n_f64(in, v, 1, span);
+            else
+                memcpy(v, in, sizeof(double) * span);
+            for (int b = 0; b < span / QK; b++)
+                q4_0_block(v + b * QK, blocks + (r * nb + s * (span / QK) + b) * 18);
         }
 }
 
