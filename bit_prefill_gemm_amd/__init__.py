@@ -10,7 +10,9 @@ Public names mirror the C ABI in include/bpg.h:
     rotate_pack_weights, quantize_act_h32, w4a4_gemm, w4a4_grouped_gemm,
     w4a4_gemm_blocksums, and the unrotated route's pack_weights_unrotated,
     quantize_act_unrotated, w4a4_gemm_unrotated; and the expert layer's glue:
-    moe_route_sort, w4a4_grouped_gemm_gather, swiglu_quantize_h32, moe_combine
+    moe_route_sort, w4a4_grouped_gemm_gather, swiglu_quantize_h32, moe_combine;
+    and rotations over 64 or 128 values: rotate_pack_weights_rot,
+    quantize_act_rot, w4a4_gemm_rot
 
 The binding is loaded lazily so that ``bit_prefill_gemm_amd.synth`` (input
 generators) imports without the HIP library.
@@ -21,6 +23,7 @@ _BINDING_NAMES = {
     "SRC_F32", "SRC_BF16", "SRC_Q4_0_ROTATED", "SRC_Q4_0", "X_F32", "X_BF16",
     "pack_weights_unrotated", "quantize_act_unrotated", "w4a4_gemm_unrotated",
     "moe_route_sort", "w4a4_grouped_gemm_gather", "swiglu_quantize_h32", "moe_combine",
+    "rotate_pack_weights_rot", "quantize_act_rot", "w4a4_gemm_rot",
 }
 
 

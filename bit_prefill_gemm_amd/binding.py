@@ -26,7 +26,8 @@ X_F32, X_BF16 = 0, 1
 ENTRY_POINTS = ("bpg_status_str", "rotate_pack_weights_bytes", "rotate_pack_weights",
                 "quantize_act_h32", "w4a4_gemm", "w4a4_grouped_gemm", "w4a4_gemm_blocksums",
                 "pack_weights_unrotated", "quantize_act_unrotated", "w4a4_gemm_unrotated",
-                "moe_route_sort", "w4a4_grouped_gemm_gather", "swiglu_quantize_h32", "moe_combine")
+                "moe_route_sort", "w4a4_grouped_gemm_gather", "swiglu_quantize_h32", "moe_combine",
+                "rotate_pack_weights_rot", "quantize_act_rot", "w4a4_gemm_rot")
 
 
 class WeightsDesc(ctypes.Structure):
@@ -77,6 +78,15 @@ def _lib_handle():
     lib.w4a4_grouped_gemm.restype = ctypes.c_int
     lib.w4a4_grouped_gemm.argtypes = [_vp, _vp, ctypes.c_int, _i64, _vp,
                                       ctypes.POINTER(WeightsDesc), _vp, _vp, _i64, _vp]
+    lib.rotate_pack_weights_rot.restype = ctypes.c_int
+    lib.rotate_pack_weights_rot.argtypes = [_vp, ctypes.c_int, _i64, _i64, _i64, ctypes.c_int, _vp,
+                                            ctypes.c_size_t, ctypes.POINTER(WeightsDesc)]
+    lib.quantize_act_rot.restype = ctypes.c_int
+    lib.quantize_act_rot.argtypes = [_vp, ctypes.c_int, _i64, _i64, _i64, ctypes.c_int, ctypes.c_int,
+                                     _vp, _vp, _vp]
+    lib.w4a4_gemm_rot.restype = ctypes.c_int
+    lib.w4a4_gemm_rot.argtypes = [_vp, _vp, ctypes.c_int, ctypes.c_int, _i64,
+                                  ctypes.POINTER(WeightsDesc), _vp, _vp, _i64, _vp]
     lib.moe_route_sort.restype = ctypes.c_int
     lib.moe_route_sort.argtypes = [_vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp]
     lib.w4a4_grouped_gemm_gather.restype = ctypes.c_int
@@ -315,4 +325,52 @@ def moe_combine(dn, slot_of, weights, tokens: int, topk: int, y=None, stream=Non
                                    tokens, topk, hidden, _dptr(y), y.stride(0),
                                    _stream_handle(stream))
     _check(st, "moe_combine")
+    return y
+
+
+# ------------------------------------------------------------------ longer rotations
+
+def rotate_pack_weights_rot(src: np.ndarray, kind: int, n: int, k: int, rotation: int,
+                            num_experts: int = 1) -> Weights:
+    src = np.ascontiguousarray(src)
+    nbytes = rotate_pack_weights_bytes(n, k, num_experts)
+    if nbytes == 0:
+        raise BpgError(2, "rotate_pack_weights_rot")
+    img = np.empty(nbytes, dtype=np.uint8)
+    desc = WeightsDesc()
+    st = _lib_handle().rotate_pack_weights_rot(src.ctypes.data_as(_vp), kind, n, k, num_experts,
+                                               rotation, img.ctypes.data_as(_vp), img.nbytes,
+                                               ctypes.byref(desc))
+    _check(st, "rotate_pack_weights_rot")
+    return Weights(desc, img)
+
+
+def quantize_act_rot(x, rotation: int, act_bits: int = 4, codes=None, scales=None, stream=None):
+    torch = _torch()
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be a 2-D tensor with unit stride along K")
+    dt = {torch.float32: X_F32, torch.bfloat16: X_BF16}.get(x.dtype)
+    if dt is None:
+        raise TypeError("x must be float32 or bfloat16")
+    m, k = x.shape
+    if codes is None:
+        codes = torch.empty((m, k // 2 if act_bits == 4 else k), dtype=torch.uint8,
+                            device=x.device)
+    if scales is None:
+        scales = torch.empty((m, k // 32), dtype=torch.float32, device=x.device)
+    st = _lib_handle().quantize_act_rot(_dptr(x), dt, m, k, x.stride(0), act_bits, rotation,
+                                        _dptr(codes), _dptr(scales), _stream_handle(stream))
+    _check(st, "quantize_act_rot")
+    return codes, scales
+
+
+def w4a4_gemm_rot(codes, scales, act_bits: int, rotation: int, w: Weights, y=None, stream=None):
+    torch = _torch()
+    m = codes.shape[0]
+    if y is None:
+        y = torch.empty((m, w.n), dtype=torch.float32, device=codes.device)
+    st = _lib_handle().w4a4_gemm_rot(_dptr(codes), _dptr(scales), act_bits, rotation, m,
+                                     ctypes.byref(w.desc), _dptr(w.image), _dptr(y), y.stride(0),
+                                     _stream_handle(stream))
+    _check(st, "w4a4_gemm_rot")
     return y

@@ -129,30 +129,29 @@ double f16_bits_to_f64(uint16_t b)
     return (double)h;
 }
 
-// In-place fp64 Walsh-Hadamard butterflies, stages h = 1..16, then times
-// fp64 1/sqrt(32) ("509 tokens a second of prompt: the Hadamard route ships",
-// section "The rotation": the weights get the same transform, once, offline).
-void rotate_block_f64(double v[32])
+// In-place fp64 Walsh-Hadamard butterflies over a span of n = 32, 64 or 128
+// values, stages h = 1 .. n/2, then times fp64 1/sqrt(n) ("509 tokens a
+// second of prompt: the Hadamard route ships", section "The rotation": the
+// weights get the same transform, once, offline; spans longer than 32 are the
+// "rotations larger than 32" of "Qwen3.8-27B at 45.7 tok/s", "What's next").
+void rotate_span_f64(double *v, int n)
 {
-    for (int h = 1; h < 32; h <<= 1)
-        for (int j = 0; j < 32; j++)
+    for (int h = 1; h < n; h <<= 1)
+        for (int j = 0; j < n; j++)
             if ((j & h) == 0) {
                 const double a = v[j], b = v[j + h];
                 v[j] = a + b;
                 v[j + h] = a - b;
             }
-    const double c = std::sqrt(2.0) / 8.0;
-    for (int i = 0; i < 32; i++)
+    // 1/sqrt(n): sqrt(2)/8, 1/8, sqrt(2)/16 (divisions by powers of two exact)
+    const double c = n == 64 ? 0.125 : (n == 128 ? std::sqrt(2.0) / 16.0 : std::sqrt(2.0) / 8.0);
+    for (int i = 0; i < n; i++)
         v[i] = v[i] * c;
 }
 
-// One Q4_0 block from 32 unrotated float weights, rotated first if `rotate`.
-void quantize_weight_block(const double in[32], bool rotate, uint8_t blk[18])
+// One Q4_0 block from 32 float weights (already rotated, if at all).
+void quantize_weight_block(const double v[32], uint8_t blk[18])
 {
-    double v[32];
-    std::memcpy(v, in, sizeof v);
-    if (rotate)
-        rotate_block_f64(v);
     double amax = 0.0;
     for (int i = 0; i < 32; i++)
         amax = std::fabs(v[i]) > amax ? std::fabs(v[i]) : amax;
@@ -215,18 +214,18 @@ size_t rotate_pack_weights_bytes(int64_t n, int64_t k, int64_t num_experts)
 
 namespace {
 
-// The packer of both routes: `rotate` selects the rotated image (stamp
-// rotation 32; sources: float weights, rotated on the way, or the Q4_0
-// tensors of a rotated file) or the unrotated one (stamp rotation 0; sources:
-// float weights or plain Q4_0 tensors).
+// The packer of every route: rot = 32 (or 64, 128) makes a rotated image
+// (stamp rotation rot; sources: float weights, rotated on the way, or the
+// Q4_0 tensors of a file rotated that way), rot = 0 the unrotated one (stamp
+// rotation 0; sources: float weights or plain Q4_0 tensors).
 bpg_status pack_image(const void *src, bpg_src_kind kind, int64_t n, int64_t k,
                       int64_t num_experts, void *dst_host, size_t dst_bytes,
-                      bpg_weights_desc *desc_out, bool rotate)
+                      bpg_weights_desc *desc_out, int rot)
 {
-    const bpg_src_kind q4_kind = rotate ? BPG_SRC_Q4_0_ROTATED : BPG_SRC_Q4_0;
+    const bpg_src_kind q4_kind = rot ? BPG_SRC_Q4_0_ROTATED : BPG_SRC_Q4_0;
     if (kind != BPG_SRC_F32 && kind != BPG_SRC_BF16 && kind != q4_kind)
         return BPG_ERR_DTYPE;
-    if (!shape_ok(n, k, num_experts))
+    if (!shape_ok(n, k, num_experts) || k % (rot > 32 ? rot : 32) != 0)
         return BPG_ERR_SHAPE;
     if (!src || !dst_host || !desc_out)
         return BPG_ERR_NULL;
@@ -241,36 +240,43 @@ bpg_status pack_image(const void *src, bpg_src_kind kind, int64_t n, int64_t k,
         std::memset(img + off, 0x88, 2048);
         std::memset(img + off + 2048, 0, 256);
     }
+    const int span = rot > 32 ? rot : 32; // values rotated together
     for (int64_t e = 0; e < num_experts; e++)
-        for (int64_t r = 0; r < n; r++)
-            for (int64_t b = 0; b < B; b++) {
-                uint8_t blk[18];
-                const int64_t row = e * n + r;
-                if (kind == q4_kind) {
-                    std::memcpy(blk, static_cast<const uint8_t *>(src) + (row * B + b) * 18, 18);
-                } else {
-                    double in[32];
-                    for (int i = 0; i < 32; i++) {
-                        const int64_t idx = row * k + b * 32 + i;
+        for (int64_t r = 0; r < n; r++) {
+            const int64_t row = e * n + r;
+            for (int64_t s0 = 0; s0 < B; s0 += span / 32) {
+                double v[128];
+                if (kind != q4_kind) {
+                    for (int i = 0; i < span; i++) {
+                        const int64_t idx = row * k + s0 * 32 + i;
                         if (kind == BPG_SRC_F32) {
-                            in[i] = (double)static_cast<const float *>(src)[idx];
+                            v[i] = (double)static_cast<const float *>(src)[idx];
                         } else {
                             const uint32_t bits = (uint32_t)static_cast<const uint16_t *>(src)[idx] << 16;
                             float f;
                             std::memcpy(&f, &bits, 4);
-                            in[i] = (double)f;
+                            v[i] = (double)f;
                         }
                     }
-                    quantize_weight_block(in, rotate, blk);
+                    if (rot)
+                        rotate_span_f64(v, span);
                 }
-                place_block(blk, e, r, b, n, G, img);
+                for (int64_t b = s0; b < s0 + span / 32; b++) {
+                    uint8_t blk[18];
+                    if (kind == q4_kind)
+                        std::memcpy(blk, static_cast<const uint8_t *>(src) + (row * B + b) * 18, 18);
+                    else
+                        quantize_weight_block(v + (b - s0) * 32, blk);
+                    place_block(blk, e, r, b, n, G, img);
+                }
             }
+        }
 
     bpg_weights_desc d;
     std::memset(&d, 0, sizeof d);
     d.magic = BPG_WEIGHTS_MAGIC;
     d.version = BPG_WEIGHTS_VERSION;
-    d.rotation = rotate ? 32 : 0;
+    d.rotation = (uint32_t)rot;
     d.layout = BPG_LAYOUT_GROUP4;
     d.n = n;
     d.k = k;
@@ -281,14 +287,15 @@ bpg_status pack_image(const void *src, bpg_src_kind kind, int64_t n, int64_t k,
     return BPG_OK;
 }
 
+// rot: span of the rotation (0 = none, 32, 64, 128)
 bpg_status quantize_checked(const void *x, bpg_x_dtype dt, int64_t m, int64_t k, int64_t ldx,
-                            int act_bits, void *codes, float *scales, void *stream, int rotate)
+                            int act_bits, void *codes, float *scales, void *stream, int rot)
 {
     if (dt != BPG_X_F32 && dt != BPG_X_BF16)
         return BPG_ERR_DTYPE;
     if (act_bits != 4 && act_bits != 8)
         return BPG_ERR_DTYPE;
-    if (m < 0 || k <= 0 || k % 32 != 0 || ldx < k || m > ((int64_t)1 << 31) - 1 ||
+    if (m < 0 || k <= 0 || k % (rot > 32 ? rot : 32) != 0 || ldx < k || m > ((int64_t)1 << 31) - 1 ||
         k > ((int64_t)1 << 30) || ldx > ((int64_t)1 << 40))
         return BPG_ERR_SHAPE;
     if (m > 0 && (!x || !codes || !scales))
@@ -298,7 +305,7 @@ bpg_status quantize_checked(const void *x, bpg_x_dtype dt, int64_t m, int64_t k,
     bpg_status s = check_device();
     if (s != BPG_OK)
         return s;
-    return launch_status(bpg::launch_quantize(x, (int)dt, m, k, ldx, act_bits, rotate, codes,
+    return launch_status(bpg::launch_quantize(x, (int)dt, m, k, ldx, act_bits, rot, codes,
                                               scales, static_cast<hipStream_t>(stream)));
 }
 
@@ -348,20 +355,20 @@ bpg_status rotate_pack_weights(const void *src, bpg_src_kind kind, int64_t n, in
                                int64_t num_experts, void *dst_host, size_t dst_bytes,
                                bpg_weights_desc *desc_out)
 {
-    return pack_image(src, kind, n, k, num_experts, dst_host, dst_bytes, desc_out, true);
+    return pack_image(src, kind, n, k, num_experts, dst_host, dst_bytes, desc_out, 32);
 }
 
 bpg_status pack_weights_unrotated(const void *src, bpg_src_kind kind, int64_t n, int64_t k,
                                   int64_t num_experts, void *dst_host, size_t dst_bytes,
                                   bpg_weights_desc *desc_out)
 {
-    return pack_image(src, kind, n, k, num_experts, dst_host, dst_bytes, desc_out, false);
+    return pack_image(src, kind, n, k, num_experts, dst_host, dst_bytes, desc_out, 0);
 }
 
 bpg_status quantize_act_h32(const void *x, bpg_x_dtype dt, int64_t m, int64_t k, int64_t ldx,
                             int act_bits, void *codes, float *scales, void *stream)
 {
-    return quantize_checked(x, dt, m, k, ldx, act_bits, codes, scales, stream, 1);
+    return quantize_checked(x, dt, m, k, ldx, act_bits, codes, scales, stream, 32);
 }
 
 bpg_status quantize_act_unrotated(const void *x, bpg_x_dtype dt, int64_t m, int64_t k,
@@ -383,6 +390,32 @@ bpg_status w4a4_gemm_unrotated(const void *codes, const float *scales, int act_b
                                int64_t ldy, void *stream)
 {
     return gemm_checked(codes, scales, act_bits, m, w, w_dev, y, ldy, stream, 0);
+}
+
+bpg_status rotate_pack_weights_rot(const void *src, bpg_src_kind kind, int64_t n, int64_t k,
+                                   int64_t num_experts, int rotation, void *dst_host,
+                                   size_t dst_bytes, bpg_weights_desc *desc_out)
+{
+    if (rotation != 32 && rotation != 64 && rotation != 128)
+        return BPG_ERR_SHAPE;
+    return pack_image(src, kind, n, k, num_experts, dst_host, dst_bytes, desc_out, rotation);
+}
+
+bpg_status quantize_act_rot(const void *x, bpg_x_dtype dt, int64_t m, int64_t k, int64_t ldx,
+                            int act_bits, int rotation, void *codes, float *scales, void *stream)
+{
+    if (rotation != 32 && rotation != 64 && rotation != 128)
+        return BPG_ERR_SHAPE;
+    return quantize_checked(x, dt, m, k, ldx, act_bits, codes, scales, stream, rotation);
+}
+
+bpg_status w4a4_gemm_rot(const void *codes, const float *scales, int act_bits, int rotation,
+                         int64_t m, const bpg_weights_desc *w, const void *w_dev, float *y,
+                         int64_t ldy, void *stream)
+{
+    if (rotation != 32 && rotation != 64 && rotation != 128)
+        return BPG_ERR_SHAPE;
+    return gemm_checked(codes, scales, act_bits, m, w, w_dev, y, ldy, stream, (uint32_t)rotation);
 }
 
 } // extern "C"

@@ -7,9 +7,10 @@
 
 namespace bpg {
 
-// Rotation + quantization of activations; dtype 0 = fp32, 1 = bf16 bits.
+// Rotation + quantization of activations; dtype 0 = fp32, 1 = bf16 bits;
+// rot = span of the rotation (0: none, 32, 64, 128; k a multiple of it).
 hipError_t launch_quantize(const void *x, int dtype, int64_t m, int64_t k, int64_t ldx,
-                           int act_bits, int rotate, void *codes, float *scales,
+                           int act_bits, int rot, void *codes, float *scales,
                            hipStream_t stream);
 // h = silu(gate) * up from gu [rows][ldgu] (gate: columns [0, inter), up:
 // [inter, 2 inter)), then rotation + quantization of h.

@@ -16,6 +16,14 @@
 // fp32(1/sqrt(32)).  The block scale is amax/7 (8-bit route: amax/127) by
 // IEEE division and the code is rint(v/d) with ties to even, clamped.
 //
+// Longer rotations ("Qwen3.8-27B at 45.7 tok/s: DFlash2 in 1bit serve, and
+// 4-bit activations with a Hadamard rotation", section "What's next": larger
+// rotations spread outliers further): with a span of 64 (128) values the two
+// (four) 32-blocks of a span sit in adjacent quads of one wave; stage h=32
+// pairs lane l with l^4 and h=64 pairs l with l^8 (ds_swizzle in XOR mode),
+// after the five stages of each block, and the factor is fp32(1/sqrt(span)).
+// The 32-value scale blocks are unchanged.
+//
 // This file must be compiled with -ffp-contract=off: no operation above may be
 // fused into an FMA, so that the codes are bit-identical to a plain
 // step-by-step evaluation.
@@ -53,6 +61,21 @@ __device__ __forceinline__ void cross_stage(float (&v)[8], bool upper)
     }
 }
 
+// The same across the quads of a span: lane l pairs with l ^ (PATTERN's XOR
+// mask); ds_swizzle bit mode, and mask 0x1F, XOR mask in bits 14:10.
+template <int PATTERN>
+__device__ __forceinline__ void cross_quad_stage(float (&v)[8], bool upper)
+{
+    const uint32_t flip = upper ? 0x80000000u : 0u;
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+        const float p = __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v[i]), PATTERN));
+        v[i] = p + __uint_as_float(__float_as_uint(v[i]) ^ flip);
+    }
+}
+constexpr int kSwzXor4 = (4 << 10) | 0x1F;
+constexpr int kSwzXor8 = (8 << 10) | 0x1F;
+
 __device__ __forceinline__ void load8(const float *src, int t, float (&v)[8])
 {
     float4 lo = *reinterpret_cast<const float4 *>(src + 4 * t);
@@ -74,13 +97,14 @@ __device__ __forceinline__ void load8(const uint16_t *src, int t, float (&v)[8])
 }
 
 // Rotate and quantize one block whose 8 values (this lane's share) are in v.
+// rot: 0 (no rotation), 32, 64 or 128 (span of the rotation).
 template <int BITS>
-__device__ __forceinline__ void quantize_block(float (&v)[8], int t, int rotate, int64_t row,
+__device__ __forceinline__ void quantize_block(float (&v)[8], int t, int rot, int64_t row,
                                                int64_t b, int64_t k, int64_t nb,
                                                uint8_t *__restrict__ codes,
                                                float *__restrict__ scales)
 {
-    if (rotate) {
+    if (rot) {
         // h = 1: pairs (4t, 4t+1), (4t+2, 4t+3) and the same in the upper half
 #pragma unroll
         for (int base = 0; base < 8; base += 4) {
@@ -106,10 +130,18 @@ __device__ __forceinline__ void quantize_block(float (&v)[8], int t, int rotate,
             v[i] = a + c;
             v[i + 4] = a - c;
         }
-        const float inv_sqrt32 = __uint_as_float(0x3E3504F3u); // fp32 nearest to 1/sqrt(32)
+        // h = 32, 64: the blocks of a longer span, in adjacent quads
+        const int lane = threadIdx.x & 63;
+        if (rot >= 64)
+            cross_quad_stage<kSwzXor4>(v, (lane & 4) != 0);
+        if (rot >= 128)
+            cross_quad_stage<kSwzXor8>(v, (lane & 8) != 0);
+        // fp32 nearest to 1/sqrt(rot): 1/sqrt(32), 1/8 and half of 1/sqrt(32)
+        const float c = rot == 64 ? 0.125f
+                                  : __uint_as_float(rot == 128 ? 0x3DB504F3u : 0x3E3504F3u);
 #pragma unroll
         for (int i = 0; i < 8; i++)
-            v[i] = v[i] * inv_sqrt32;
+            v[i] = v[i] * c;
     }
 
     float amax = 0.0f;
@@ -171,7 +203,7 @@ __device__ __forceinline__ void quantize_block(float (&v)[8], int t, int rotate,
 // so the quad-local DPP exchanges never read an exited lane.
 template <typename T, int BITS>
 __global__ __launch_bounds__(kThreads) void quantize_h32_kernel(
-    const T *__restrict__ x, int64_t k, int64_t ldx, int64_t nblk_total, int rotate,
+    const T *__restrict__ x, int64_t k, int64_t ldx, int64_t nblk_total, int rot,
     uint8_t *__restrict__ codes, float *__restrict__ scales)
 {
     const int t = threadIdx.x & 3;
@@ -191,7 +223,7 @@ __global__ __launch_bounds__(kThreads) void quantize_h32_kernel(
             row = next / nb;
             load8(x + row * ldx + (next - row * nb) * 32, t, nv);
         }
-        quantize_block<BITS>(v, t, rotate, cur_row, cur_b, k, nb, codes, scales);
+        quantize_block<BITS>(v, t, rot, cur_row, cur_b, k, nb, codes, scales);
         if (next >= nblk_total)
             break;
         blk = next;
@@ -255,7 +287,7 @@ __global__ __launch_bounds__(kThreads) void swiglu_quantize_kernel(
 #pragma unroll
         for (int i = 0; i < 8; i++)
             v[i] = silu_f32(g[i]) * u[i];
-        quantize_block<BITS>(v, t, 1, row, b, inter, nb, codes, scales);
+        quantize_block<BITS>(v, t, 32, row, b, inter, nb, codes, scales);
     }
 }
 
@@ -278,7 +310,7 @@ hipError_t launch_swiglu_quantize(const float *gu, int64_t rows, int64_t inter, 
 }
 
 hipError_t launch_quantize(const void *x, int dtype, int64_t m, int64_t k, int64_t ldx,
-                           int act_bits, int rotate, void *codes, float *scales,
+                           int act_bits, int rot, void *codes, float *scales,
                            hipStream_t stream)
 {
     const int64_t nblk = m * (k / 32);
@@ -290,16 +322,16 @@ hipError_t launch_quantize(const void *x, int dtype, int64_t m, int64_t k, int64
     uint8_t *c = static_cast<uint8_t *>(codes);
     if (dtype == 0 && act_bits == 4)
         quantize_h32_kernel<float, 4><<<grid, kThreads, 0, stream>>>(
-            static_cast<const float *>(x), k, ldx, nblk, rotate, c, scales);
+            static_cast<const float *>(x), k, ldx, nblk, rot, c, scales);
     else if (dtype == 0)
         quantize_h32_kernel<float, 8><<<grid, kThreads, 0, stream>>>(
-            static_cast<const float *>(x), k, ldx, nblk, rotate, c, scales);
+            static_cast<const float *>(x), k, ldx, nblk, rot, c, scales);
     else if (act_bits == 4)
         quantize_h32_kernel<uint16_t, 4><<<grid, kThreads, 0, stream>>>(
-            static_cast<const uint16_t *>(x), k, ldx, nblk, rotate, c, scales);
+            static_cast<const uint16_t *>(x), k, ldx, nblk, rot, c, scales);
     else
         quantize_h32_kernel<uint16_t, 8><<<grid, kThreads, 0, stream>>>(
-            static_cast<const uint16_t *>(x), k, ldx, nblk, rotate, c, scales);
+            static_cast<const uint16_t *>(x), k, ldx, nblk, rot, c, scales);
     return hipGetLastError();
 }
 

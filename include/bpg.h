@@ -110,7 +110,9 @@ typedef struct {
     uint32_t magic;        /* BPG_WEIGHTS_MAGIC */
     uint32_t version;      /* BPG_WEIGHTS_VERSION */
     uint32_t rotation;     /* 32: every block rotated by H32 (rotate_pack_weights);
-                              0: unrotated (pack_weights_unrotated) */
+                              0: unrotated (pack_weights_unrotated);
+                              64, 128: spans rotated by H64, H128
+                              (rotate_pack_weights_rot) */
     uint32_t layout;       /* BPG_LAYOUT_GROUP4 */
     int64_t n;             /* output channels per expert */
     int64_t k;             /* input channels */
@@ -196,6 +198,37 @@ bpg_status quantize_act_unrotated(const void *x, bpg_x_dtype dt, int64_t m, int6
 bpg_status w4a4_gemm_unrotated(const void *codes, const float *scales, int act_bits, int64_t m,
                                const bpg_weights_desc *w, const void *w_dev, float *y,
                                int64_t ldy, void *stream);
+
+/*
+ * Rotations longer than 32 ("Qwen3.8-27B at 45.7 tok/s: DFlash2 in 1bit
+ * serve, and 4-bit activations with a Hadamard rotation", section "What's
+ * next": rotations larger than 32, which spread outliers further).  The span
+ * of the rotation is `rotation` = 32, 64 or 128 values (Sylvester order,
+ * butterflies h = 1 .. rotation/2 in the 32-point route's order and sign
+ * convention, then times 1/sqrt(rotation): fp32(1/sqrt 32), 1/8 or half of
+ * fp32(1/sqrt 32) on the GPU, the fp64 value offline); the 32-value scale
+ * blocks, the codes and the image layout are unchanged.  K must be a multiple
+ * of the span.  With rotation = 32 these are exactly rotate_pack_weights,
+ * quantize_act_h32 and w4a4_gemm.
+ *
+ * rotate_pack_weights_rot: float sources are rotated per span in fp64 and
+ * quantized to Q4_0; BPG_SRC_Q4_0_ROTATED blocks (rotated with this span) are
+ * only re-laid out; the stamp records the span.  Errors: NULL, SHAPE (also
+ * for a span other than 32, 64, 128), DTYPE, BUFFER.
+ * quantize_act_rot: as quantize_act_h32 with the given span.
+ * Errors: NULL, SHAPE, ALIGN, DTYPE, DEVICE, LAUNCH.
+ * w4a4_gemm_rot: as w4a4_gemm for codes made with the given span; the image's
+ * stamp must record the same span (else STAMP).
+ * Errors: NULL, SHAPE, ALIGN, DTYPE, STAMP, DEVICE, LAUNCH.
+ */
+bpg_status rotate_pack_weights_rot(const void *src, bpg_src_kind kind, int64_t n, int64_t k,
+                                   int64_t num_experts, int rotation, void *dst_host,
+                                   size_t dst_bytes, bpg_weights_desc *desc_out);
+bpg_status quantize_act_rot(const void *x, bpg_x_dtype dt, int64_t m, int64_t k, int64_t ldx,
+                            int act_bits, int rotation, void *codes, float *scales, void *stream);
+bpg_status w4a4_gemm_rot(const void *codes, const float *scales, int act_bits, int rotation,
+                         int64_t m, const bpg_weights_desc *w, const void *w_dev, float *y,
+                         int64_t ldy, void *stream);
 
 /*
  * Dense W4A4 (or W4A8) product y = x . W^T from codes, on the GPU

@@ -300,3 +300,31 @@ def test_combine_errors():
     assert f(dn=MIS) == ALIGN and f(lddn=66) == ALIGN and f(w=ctypes.c_void_p(0x100002)) == ALIGN
     if not os.path.exists("/dev/kfd"):
         assert f() == DEVICE
+
+
+# ------------------------------------------------------------ longer rotations
+
+def test_rotation_length_errors():
+    lib = bb.lib()
+    d = bb.WeightsDesc()
+    src = np.zeros(64 * 8 * 18, dtype=np.uint8)
+    dst = np.zeros(64 * 8 * 18, dtype=np.uint8)
+    sp, dp = src.ctypes.data_as(ctypes.c_void_p), dst.ctypes.data_as(ctypes.c_void_p)
+    for r in (0, 16, 96, 256):
+        assert lib.rotate_pack_weights_rot(sp, 2, 64, 256, 1, r, dp, dst.nbytes, ctypes.byref(d)) == SHAPE
+        assert lib.quantize_act_rot(P, 0, 4, 256, 256, 4, r, P2, P, NUL) == SHAPE
+    # K must be a multiple of the span
+    assert lib.rotate_pack_weights_rot(sp, 0, 64, 160, 1, 64, dp, dst.nbytes, ctypes.byref(d)) == SHAPE
+    assert lib.quantize_act_rot(P, 0, 4, 192, 192, 4, 128, P2, P, NUL) == SHAPE
+    assert lib.rotate_pack_weights_rot(sp, 3, 64, 256, 1, 64, dp, dst.nbytes, ctypes.byref(d)) == DTYPE
+    assert lib.rotate_pack_weights_rot(sp, 2, 64, 256, 1, 128, dp, dst.nbytes, ctypes.byref(d)) == OK
+    assert d.rotation == 128
+    # the product checks the span against the stamp
+    dd = _desc_with(rotation=128)
+    g = lambda r, desc: lib.w4a4_gemm_rot(P, P2, 4, r, 4, ctypes.byref(desc), P, P2, 64, NUL)
+    assert g(64, dd) == STAMP and g(96, dd) == SHAPE
+    assert gemm(desc=dd) == STAMP
+    if not os.path.exists("/dev/kfd"):
+        assert g(128, dd) == DEVICE
+        assert g(32, good_desc()) == DEVICE
+        assert lib.quantize_act_rot(P, 0, 4, 256, 256, 4, 64, P2, P, NUL) == DEVICE

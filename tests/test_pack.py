@@ -114,3 +114,23 @@ def test_unrotated_float_source_matches_oracle_bit_exact(dtype):
     # and the two routes differ: the rotated image holds other blocks
     R = bb.rotate_pack_weights(src, kind, n, k, e)
     assert not np.array_equal(unpack_image(R.image, n, k, e).reshape(e * n, k // 32, 18), got)
+
+
+# ------------------------------------------------------------ longer rotations
+
+@pytest.mark.parametrize("rot", [32, 64, 128])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_rot_float_source_matches_oracle_bit_exact(rot, dtype):
+    rng = np.random.default_rng(rot + len(dtype))
+    n, k, e = 64, 384, 2
+    w = synth.draw_weights_f32(rng, e * n, k, 0.03)
+    w[:, rng.choice(k, 4, replace=False)] *= 15.0
+    src = w if dtype == "f32" else synth.bf16_bits(w)
+    kind = bb.SRC_F32 if dtype == "f32" else bb.SRC_BF16
+    W = bb.rotate_pack_weights_rot(src, kind, n, k, rot, e)
+    assert W.desc.rotation == rot
+    got = unpack_image(W.image, n, k, e).reshape(e * n, k // 32, 18)
+    assert np.array_equal(got, oracle.quantize_weights_q4_0_rot(src, rot))
+    if rot == 32:
+        R = bb.rotate_pack_weights(src, kind, n, k, e)
+        assert np.array_equal(R.image, W.image)
