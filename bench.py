@@ -20,7 +20,7 @@ weighted combine; `kernel_us` gives each kernel's own duration).
 Prints ONE JSON line.  `value` is prompt tokens per second of the step.  The
 `roofline` object covers the GEMM kernel (the dominant kernel).  Its average
 duration is measured with HIP events recorded on the launch stream around
-every GEMM in the timed region.  The bound is whichever algorithmic floor is
+every 8th GEMM of the timed region.  The bound is whichever algorithmic floor is
 larger: the fp32 VALU epilogue (two FMAs per output element and 32-block)
 against the fp32 vector peak (dense shapes with many rows), or the HBM bytes
 against the HBM peak (a few rows, and the grouped expert GEMMs, whose weight
@@ -78,6 +78,8 @@ WORKLOADS = {
 # weight-stream kernel used for a few rows)
 GEMM_SRCS = [os.path.join(ROOT, "bit_prefill_gemm_amd", "csrc", f) for f in ("gemm.hip", "skinny.hip", "wide.hip", "operands.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_traffic.json")
+# timed steps between two whose GEMM is bracketed by events
+EVENT_EVERY = 8
 
 
 def parse():
@@ -225,24 +227,28 @@ def main():
         else:
             bb.w4a4_grouped_gemm(codes, scales, bits, offsets, Ws[j], y=y, stream=stream)
 
-    # The timed steps record two events per step, around the GEMM only (each
-    # event is one more packet on the queue; a third around the quantizer
-    # added ~3 us per step).  The quantizer's own duration is taken after the
-    # timed region, with events around it alone.
+    # The GEMM's duration is taken with two events around it on every
+    # EVENT_EVERY-th timed step: each recorded event is one more packet on the
+    # queue and costs the step several microseconds, so recording them on
+    # every step would inflate the step time.  The quantizer's own duration
+    # is taken after the timed region, with events around it alone.
     with torch.cuda.stream(stream):
         for i in range(args.warmup):
             quantize(i % copies)
             gemm(i % copies)
         torch.cuda.synchronize()
         evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(2))
-               for _ in range(args.steps)]
+               for _ in range(0, args.steps, EVENT_EVERY)]
         t0 = time.perf_counter()
         for i in range(args.steps):
             j = (args.warmup + i) % copies
             quantize(j)
-            evs[i][0].record(stream)
-            gemm(j)
-            evs[i][1].record(stream)
+            if i % EVENT_EVERY == 0:
+                evs[i // EVENT_EVERY][0].record(stream)
+                gemm(j)
+                evs[i // EVENT_EVERY][1].record(stream)
+            else:
+                gemm(j)
         torch.cuda.synchronize()
         t1 = time.perf_counter()
         qevs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(2))
@@ -363,17 +369,27 @@ def main_layer(args, wl):
         "moe_combine": lambda j: bb.moe_combine(dn, slot_of, weights, T, K8, y=y, stream=stream),
     }
 
-    def step(j):
-        for f in kernels.values():
-            f(j)
+    gate_name = "w4a4_grouped_gemm_gather"
+
+    def step(j, ev=None):
+        for name, f in kernels.items():
+            if ev is not None and name == gate_name:
+                ev[0].record(stream)
+                f(j)
+                ev[1].record(stream)
+            else:
+                f(j)
 
     with torch.cuda.stream(stream):
         for i in range(args.warmup):
             step(i % copies)
         torch.cuda.synchronize()
+        gate_evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(2))
+                    for _ in range(0, args.steps, EVENT_EVERY)]
         t0 = time.perf_counter()
         for i in range(args.steps):
-            step((args.warmup + i) % copies)
+            step((args.warmup + i) % copies,
+                 gate_evs[i // EVENT_EVERY] if i % EVENT_EVERY == 0 else None)
         torch.cuda.synchronize()
         t1 = time.perf_counter()
         # each kernel's own duration: event pairs around it alone, in step order
@@ -391,7 +407,7 @@ def main_layer(args, wl):
     kernel_us = {name: 1e3 * float(np.mean([a.elapsed_time(b) for a, b in v]))
                  for name, v in evs.items()}
     ms_per_step = (t1 - t0) * 1e3 / args.steps
-    gate_s = kernel_us["w4a4_grouped_gemm_gather"] * 1e-6
+    gate_s = float(np.mean([a.elapsed_time(b) for a, b in gate_evs])) * 1e-3
     roofline = roofline_of("w4a4_grouped_gemm_gather", rows, H, 2 * I, bits, E, gate_s, None)
     out = {
         "metric": "prompt tokens/s + effective TOPS (% int8 MFMA peak) for rotated W4A4 GEMM, M=512",

@@ -42,9 +42,10 @@ bpg_status check_device()
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// expert sort: one workgroup, LDS of (1 + 16) ints per expert
+// expert sort: one workgroup per expert, each reading every entry (sized for
+// prompt batches)
 constexpr int64_t kMaxSortExperts = 512;
-constexpr int64_t kMaxSortEntries = (int64_t)1 << 24;
+constexpr int64_t kMaxSortEntries = (int64_t)1 << 20;
 
 bpg_status launch_status(hipError_t e) { return e == hipSuccess ? BPG_OK : BPG_ERR_LAUNCH; }
 

@@ -17,91 +17,83 @@ namespace bpg {
 
 namespace {
 
-constexpr int kSortThreads = 1024;  // one workgroup: 16 waves
-constexpr int kSortWaves = kSortThreads / 64;
+constexpr int kSortThreads = 256;
 
-// Counting sort in one workgroup.  Pass 1 counts the entries per expert (LDS
-// atomics: the totals do not depend on their order) and scans the counts into
-// offsets.  Pass 2 walks the entries in chunks of 1024, one per thread; inside
-// a wave every lane finds how many lower lanes hold its expert with ballots
-// (one round per distinct expert in the wave, at most 64), the per-wave
-// counts are scanned across the 16 waves per expert, and each entry lands at
-// offset + earlier chunks + earlier waves + earlier lanes: the stable order.
+// Inclusive scan of one int per thread over the workgroup (kSortThreads),
+// in thread order; `wsum` is LDS of kSortThreads / 64 ints.
+__device__ __forceinline__ int block_scan_incl(int v, int *wsum)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int incl = v;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int u = __shfl_up(incl, d);
+        if (lane >= d)
+            incl += u;
+    }
+    if (lane == 63)
+        wsum[wave] = incl;
+    __syncthreads();
+    int before = 0;
+    for (int w = 0; w < wave; w++)
+        before += wsum[w];
+    __syncthreads();
+    return before + incl;
+}
+
+// Counting sort with one workgroup per expert x.  Every workgroup counts the
+// entries of every expert (LDS atomics: the totals do not depend on their
+// order) to find x's offset; thread t owns the contiguous entry range
+// [t*per, (t+1)*per), counts its entries of expert x, and a scan over the
+// threads in order gives each such entry its place: the stable order.
 // Expert ids outside [0, experts) are clamped (the rows stay in bounds).
 __global__ __launch_bounds__(kSortThreads) void route_sort_kernel(
     const int32_t *__restrict__ expert_of, int n, int topk, int experts,
     int32_t *__restrict__ offsets, int32_t *__restrict__ row_token, int32_t *__restrict__ slot_of)
 {
-    extern __shared__ int32_t sh[];
-    int32_t *base = sh;                   // [experts]: next free position
-    int32_t *wcnt = sh + experts;         // [kSortWaves][experts]
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    extern __shared__ int32_t hist[]; // [experts], then kSortThreads / 64 ints
+    int *wsum = hist + experts;
+    const int x = blockIdx.x, tid = threadIdx.x;
+    const int per = (n + kSortThreads - 1) / kSortThreads;
+    const int lo = tid * per, hi = lo + per < n ? lo + per : n;
+    auto expert_at = [&](int i) {
+        const int e = expert_of[i];
+        return e < 0 ? 0 : (e >= experts ? experts - 1 : e);
+    };
 
     for (int e = tid; e < experts; e += kSortThreads)
-        base[e] = 0;
+        hist[e] = 0;
     __syncthreads();
-    for (int i = tid; i < n; i += kSortThreads) {
-        int e = expert_of[i];
-        e = e < 0 ? 0 : (e >= experts ? experts - 1 : e);
-        atomicAdd(&base[e], 1);
+    int mine = 0; // entries of expert x in this thread's range
+    for (int i = lo; i < hi; i++) {
+        const int e = expert_at(i);
+        atomicAdd(&hist[e], 1);
+        mine += e == x;
     }
     __syncthreads();
+    // offset of x: the entries of the experts before it
+    int part = 0;
+    for (int e = tid; e < x; e += kSortThreads)
+        part += hist[e];
+    const int offset = block_scan_incl(part, wsum);
+    __shared__ int off_sh;
+    if (tid == kSortThreads - 1)
+        off_sh = offset;
+    __syncthreads();
+    const int base_x = off_sh;
     if (tid == 0) {
-        int run = 0;
-        for (int e = 0; e < experts; e++) {
-            const int c = base[e];
-            offsets[e] = run;
-            base[e] = run;
-            run += c;
-        }
-        offsets[experts] = run;
+        offsets[x] = base_x;
+        if (x == experts - 1)
+            offsets[experts] = base_x + hist[x];
     }
-    __syncthreads();
-
-    for (int c0 = 0; c0 < n; c0 += kSortThreads) {
-        for (int i = tid; i < kSortWaves * experts; i += kSortThreads)
-            wcnt[i] = 0;
-        __syncthreads();
-        const int idx = c0 + tid;
-        const bool valid = idx < n;
-        int e = 0;
-        if (valid) {
-            e = expert_of[idx];
-            e = e < 0 ? 0 : (e >= experts ? experts - 1 : e);
+    // places of this thread's entries of expert x
+    int pos = base_x + block_scan_incl(mine, wsum) - mine;
+    for (int i = lo; i < hi; i++)
+        if (expert_at(i) == x) {
+            slot_of[i] = pos;
+            row_token[pos] = i / topk;
+            pos++;
         }
-        // rank among the lower lanes of this wave with the same expert
-        uint64_t left = __ballot(valid);
-        int rank = 0;
-        while (left != 0) { // uniform: every lane sees the same mask
-            const int leader = __builtin_ctzll(left);
-            const int x = __builtin_amdgcn_readlane(e, leader);
-            const uint64_t same = __ballot(valid && e == x) & left;
-            if (valid && e == x) {
-                rank = __builtin_popcountll(same & ((1ull << lane) - 1ull));
-                if (lane == leader)
-                    wcnt[wave * experts + x] = __builtin_popcountll(same);
-            }
-            left &= ~same;
-        }
-        __syncthreads();
-        // per expert: exclusive scan over the waves, then advance the base
-        for (int x = tid; x < experts; x += kSortThreads) {
-            int run = base[x];
-            for (int w = 0; w < kSortWaves; w++) {
-                const int cnt = wcnt[w * experts + x];
-                wcnt[w * experts + x] = run;
-                run += cnt;
-            }
-            base[x] = run;
-        }
-        __syncthreads();
-        if (valid) {
-            const int pos = wcnt[wave * experts + e] + rank;
-            slot_of[idx] = pos;
-            row_token[pos] = idx / topk;
-        }
-        __syncthreads();
-    }
 }
 
 // y[t][c..c+3] = sum_j w[t k + j] * dn[slot[t k + j]][c..c+3], j ascending,
@@ -136,9 +128,9 @@ hipError_t launch_route_sort(const int32_t *expert_of, int64_t tokens, int64_t t
                              int64_t experts, int32_t *offsets, int32_t *row_token,
                              int32_t *slot_of, hipStream_t stream)
 {
-    const size_t lds = (size_t)(1 + kSortWaves) * experts * sizeof(int32_t);
-    route_sort_kernel<<<1, kSortThreads, lds, stream>>>(expert_of, (int)(tokens * topk), (int)topk,
-                                                        (int)experts, offsets, row_token, slot_of);
+    const size_t lds = ((size_t)experts + kSortThreads / 64) * sizeof(int32_t);
+    route_sort_kernel<<<dim3((unsigned)experts), kSortThreads, lds, stream>>>(
+        expert_of, (int)(tokens * topk), (int)topk, (int)experts, offsets, row_token, slot_of);
     return hipGetLastError();
 }
 

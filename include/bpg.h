@@ -278,14 +278,14 @@ bpg_status w4a4_grouped_gemm(const void *codes, const float *scales, int act_bit
  *   -> moe_combine.
  *
  * moe_route_sort: sorts the entries by expert, stably (entry order inside an
- * expert), on the GPU, in one workgroup.
+ * expert), on the GPU (one workgroup per expert, each reading every entry).
  *   expert_of_dev   device, int32 [tokens*topk]; ids outside [0, experts) are
  *                   clamped (unspecified grouping, in-bounds accesses)
  *   offsets_dev     device, int32 [experts+1]: expert e owns sorted rows
  *                   [offsets[e], offsets[e+1])
  *   row_token_dev   device, int32 [tokens*topk]: the token of each sorted row
  *   slot_of_dev     device, int32 [tokens*topk]: the sorted row of each entry
- * Limits: experts <= 512, tokens*topk <= 2^24.  Pointers 4-byte aligned.
+ * Limits: experts <= 512, tokens*topk <= 2^20.  Pointers 4-byte aligned.
  * Errors: NULL, SHAPE, ALIGN, DEVICE, LAUNCH.
  */
 bpg_status moe_route_sort(const int32_t *expert_of_dev, int64_t tokens, int64_t topk,
