@@ -76,7 +76,7 @@ WORKLOADS = {
 }
 # kernel sources of the GEMM paths (the tiled and grouped kernels, and the
 # weight-stream kernel used for a few rows)
-GEMM_SRCS = [os.path.join(ROOT, "bit_prefill_gemm_amd", "csrc", f) for f in ("gemm.hip", "skinny.hip", "wide.hip", "operands.h")]
+GEMM_SRCS = [os.path.join(ROOT, "bit_prefill_gemm_amd", "csrc", f) for f in ("gemm.hip", "skinny.hip", "wide.hip", "grouped.hip", "operands.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_traffic.json")
 # timed steps between two whose GEMM is bracketed by events
 EVENT_EVERY = 8

@@ -749,6 +749,8 @@ hipError_t launch_grouped_gemm(const GemmProblem &p, hipStream_t stream)
 {
     if (p.rows == 0)
         return hipSuccess;
+    if (grouped_wide_fits(p))
+        return launch_grouped_wide(p, stream);
     return p.act_bits == 4 ? launch_grouped_bits<4>(p, stream) : launch_grouped_bits<8>(p, stream);
 }
 

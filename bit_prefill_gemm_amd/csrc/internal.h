@@ -55,6 +55,10 @@ hipError_t launch_skinny(const GemmProblem &p, hipStream_t stream);
 // tiles, tn = 4 or 5; usable when wide_fits(p, tn).
 bool wide_fits(const GemmProblem &p, int tn);
 hipError_t launch_wide(const GemmProblem &p, int tn, hipStream_t stream);
+// The grouped kernel on 64-row expert slots (4-bit activations, n a multiple
+// of 128, at most 1024 experts): usable when grouped_wide_fits(p).
+bool grouped_wide_fits(const GemmProblem &p);
+hipError_t launch_grouped_wide(const GemmProblem &p, hipStream_t stream);
 hipError_t launch_grouped_gemm(const GemmProblem &p, hipStream_t stream);
 hipError_t launch_blocksums(const GemmProblem &p, hipStream_t stream);
 

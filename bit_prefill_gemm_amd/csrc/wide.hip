@@ -36,29 +36,6 @@ namespace bpg {
 
 namespace {
 
-typedef __attribute__((address_space(3))) void lds_void;
-typedef const __attribute__((address_space(1))) void glb_void;
-
-// An integer the optimizer cannot take apart.  LDS addresses built as
-// "array + opaque offset" stay one step from their array, which lets the
-// compiler attribute every read to its buffer and so not wait for the direct
-// loads into the other buffer before it.
-__device__ __forceinline__ uint32_t opaque(uint32_t x)
-{
-    asm("" : "+v"(x));
-    return x;
-}
-
-// The same address in every lane, held in scalar registers (a direct load
-// then takes it as its scalar base and the lane offset as a 32-bit register).
-__device__ __forceinline__ const uint8_t *uniform(const uint8_t *ptr)
-{
-    const uint64_t a = reinterpret_cast<uint64_t>(ptr);
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
-    return reinterpret_cast<const uint8_t *>(((uint64_t)hi << 32) | lo);
-}
-
 template <int TN_>
 struct WideCfg {
     static constexpr int TN = TN_;                   // 32-column tiles per workgroup
