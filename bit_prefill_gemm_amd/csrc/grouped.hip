@@ -37,6 +37,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "internal.h"
 #include "operands.h"
 
@@ -340,9 +342,13 @@ __global__ __launch_bounds__(256, 2) void grouped_kernel(GemmProblem p, int tile
 
     // 32 rows (byte offsets ah, dh: rows 0..31 or 32..63) of the wave's tile
     // over the stage's eight blocks; the matrix instruction of block q+1 is
-    // issued before the epilogue of block q
-    auto compute = [&](float (&acc)[16], const uint8_t *buf, uint32_t ah, uint32_t dh)
-        __attribute__((always_inline)) {
+    // issued before the epilogue of block q.  Result register r of a lane
+    // holds row 8 (r / 4) + 4 hk + r % 4: with ng = 1 (compiled in) only the
+    // first 8-row group gets an epilogue, for a second pass whose rows all
+    // lie in it (the common case: an expert slot of 33..40 rows).
+    auto compute = [&](auto ng_tag, float (&acc)[16], const uint8_t *buf, uint32_t ah,
+                       uint32_t dh) __attribute__((always_inline)) {
+        constexpr int ng = decltype(ng_tag)::value;
         uint4 wr[2][2];
         uint2 hw[2];
 #pragma unroll
@@ -368,7 +374,7 @@ __global__ __launch_bounds__(256, 2) void grouped_kernel(GemmProblem p, int tile
                 a[2] = (int)act_hi(ad.x);
                 a[3] = (int)act_hi(ad.y);
 #pragma unroll
-                for (int r4 = 0; r4 < 4; r4++)
+                for (int r4 = 0; r4 < ng; r4++)
                     dac[r4] = *reinterpret_cast<const float4 *>(
                         buf + (dh + d_rd + q * 256 + r4 * 32));
                 const int g = q >> 2, qq = q & 3;
@@ -388,7 +394,7 @@ __global__ __launch_bounds__(256, 2) void grouped_kernel(GemmProblem p, int tile
             }
             if (q > 0) {
 #pragma unroll
-                for (int r4 = 0; r4 < 4; r4++) {
+                for (int r4 = 0; r4 < ng; r4++) {
                     const float dq[4] = {dap[r4].x, dap[r4].y, dap[r4].z, dap[r4].w};
 #pragma unroll
                     for (int e = 0; e < 4; e++) {
@@ -402,7 +408,7 @@ __global__ __launch_bounds__(256, 2) void grouped_kernel(GemmProblem p, int tile
             dwp = dwc;
             nbp = nbc;
 #pragma unroll
-            for (int r4 = 0; r4 < 4; r4++)
+            for (int r4 = 0; r4 < ng; r4++)
                 dap[r4] = dac[r4];
             // one block at a time: hoisting later blocks' matrix instructions
             // above these epilogues keeps all their results live at once
@@ -464,9 +470,13 @@ __global__ __launch_bounds__(256, 2) void grouped_kernel(GemmProblem p, int tile
         // the source rows of item kc + 2 replace those of item kc
         if (gather && stc == 0 && wave == 0 && kc + 2 < nmine)
             fetch_ids((kc & 1) ? ids1 : ids0, kc + 2);
-        compute(acc_lo, bc, 0u, 0u);
-        if (ccur.rows > 32)
-            compute(acc_hi, bc, 32u * 128u, 32u * 4u);
+        typedef std::integral_constant<int, 1> OneGroup;
+        typedef std::integral_constant<int, 4> AllGroups;
+        compute(AllGroups{}, acc_lo, bc, 0u, 0u);
+        if (ccur.rows > 40)
+            compute(AllGroups{}, acc_hi, bc, 32u * 128u, 32u * 4u);
+        else if (ccur.rows > 32)
+            compute(OneGroup{}, acc_hi, bc, 32u * 128u, 32u * 4u);
         __builtin_amdgcn_s_waitcnt(0x0F70); // vmcnt(0): the next pair has landed
         __syncthreads();
         if (++stc < nst)
