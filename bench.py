@@ -89,6 +89,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="attn512", choices=sorted(WORKLOADS))
     ap.add_argument("--bits", type=int, default=4, choices=(4, 8))
+    ap.add_argument("--out", default="f32", choices=("f32", "bf16"),
+                    help="output type of the GEMM (bf16: the rounded-output entry points)")
     ap.add_argument("--cold-bytes", type=float, default=512e6,
                     help="total bytes of distinct input copies cycled through")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -97,9 +99,10 @@ def parse():
     return ap.parse_args()
 
 
-def gemm_bytes(m, k, n, bits, experts=1):
-    """Algorithmic HBM bytes of one GEMM: weight image, codes, scales, fp32 output."""
-    return experts * n * k * 18 // 32 + m * k * bits // 8 + m * (k // 32) * 4 + m * n * 4
+def gemm_bytes(m, k, n, bits, experts=1, out_bytes=4):
+    """Algorithmic HBM bytes of one GEMM: weight image, codes, scales, output (fp32: 4 bytes
+    an element, bf16: 2)."""
+    return experts * n * k * 18 // 32 + m * k * bits // 8 + m * (k // 32) * 4 + m * n * out_bytes
 
 
 def source_hash():
@@ -109,7 +112,7 @@ def source_hash():
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload, bits):
+def measured_traffic(workload, bits, out="f32"):
     """HBM bytes per GEMM launch from the committed counter summary, if still current."""
     try:
         rec = json.load(open(TRAFFIC_FILE))
@@ -117,7 +120,7 @@ def measured_traffic(workload, bits):
         return None
     if rec.get("gemm_source_sha256_16") != source_hash():
         return None
-    e = rec.get("workloads", {}).get("%s/%d" % (workload, bits))
+    e = rec.get("workloads", {}).get("%s/%d%s" % (workload, bits, "" if out == "f32" else "/" + out))
     if not e:
         return None
     return e["fetch_bytes"] + e["write_bytes"]
@@ -151,11 +154,11 @@ def cpu_baseline(data, wl, name, bits, seconds):
                       "output), %d repetition(s) in %.1f s" % (name, m, k, m, k, n, reps, el)}
 
 
-def roofline_of(kernel, m, k, n, bits, experts, seconds, traffic):
+def roofline_of(kernel, m, k, n, bits, experts, seconds, traffic, out_bytes=4):
     """The binding roofline of one GEMM launch: whichever algorithmic floor is
     larger, the HBM bytes at 8 TB/s or the fp32 epilogue (two FMAs per output
     and block) at the fp32 vector peak."""
-    gbytes = gemm_bytes(m, k, n, bits, experts)
+    gbytes = gemm_bytes(m, k, n, bits, experts, out_bytes)
     epi_flops = 4.0 * m * n * (k // 32)
     if gbytes / PEAK_HBM >= epi_flops / PEAK_FP32_FLOPS:
         return {"bound": "hbm", "achieved": gbytes / seconds / 1e9, "peak": PEAK_HBM / 1e9,
@@ -215,7 +218,9 @@ def main():
     Ws = [bb.Weights(W0.desc, im) for im in imgs]
     codes = torch.empty((m, k // 2 if bits == 4 else k), dtype=torch.uint8, device=dev)
     scales = torch.empty((m, k // 32), dtype=torch.float32, device=dev)
-    y = torch.empty((m, n), dtype=torch.float32, device=dev)
+    bf16_out = args.out == "bf16"
+    out_bytes = 2 if bf16_out else 4
+    y = torch.empty((m, n), dtype=torch.bfloat16 if bf16_out else torch.float32, device=dev)
     stream = torch.cuda.Stream(device=dev)
 
     def quantize(j):
@@ -223,9 +228,11 @@ def main():
 
     def gemm(j):
         if offsets is None:
-            bb.w4a4_gemm(codes, scales, bits, Ws[j], y=y, stream=stream)
+            f = bb.w4a4_gemm_bf16 if bf16_out else bb.w4a4_gemm
+            f(codes, scales, bits, Ws[j], y=y, stream=stream)
         else:
-            bb.w4a4_grouped_gemm(codes, scales, bits, offsets, Ws[j], y=y, stream=stream)
+            f = bb.w4a4_grouped_gemm_bf16 if bf16_out else bb.w4a4_grouped_gemm
+            f(codes, scales, bits, offsets, Ws[j], y=y, stream=stream)
 
     # The GEMM's duration is taken with two events around it on every
     # EVENT_EVERY-th timed step: each recorded event is one more packet on the
@@ -265,11 +272,11 @@ def main():
     gemm_s = gemm_ms * 1e-3
     ops = 2.0 * m * n * k
     eff_tops = ops / gemm_s / 1e12
-    gbytes = gemm_bytes(m, k, n, bits, experts)
-    traffic = measured_traffic(args.workload, bits)
+    gbytes = gemm_bytes(m, k, n, bits, experts, out_bytes)
+    traffic = measured_traffic(args.workload, bits, args.out)
 
-    kernel = "w4a4_gemm" if experts == 1 else "w4a4_grouped_gemm"
-    roofline = roofline_of(kernel, m, k, n, bits, experts, gemm_s, traffic)
+    kernel = ("w4a4_gemm" if experts == 1 else "w4a4_grouped_gemm") + ("_bf16" if bf16_out else "")
+    roofline = roofline_of(kernel, m, k, n, bits, experts, gemm_s, traffic, out_bytes)
 
     out = {
         "metric": "prompt tokens/s + effective TOPS (% int8 MFMA peak) for rotated W4A4 GEMM, M=512",
@@ -289,7 +296,7 @@ def main():
                                % (args.workload, m, k, n,
                                   ", %d experts (grouped)" % experts if experts > 1 else "", bits),
                    "m": m, "k": k, "n": n, "experts": experts, "act_bits": bits,
-                   "cold_copies": copies},
+                   "out": args.out, "cold_copies": copies},
         "roofline": roofline,
         "int8_mfma": {"achieved": eff_tops, "peak": PEAK_INT8_OPS / 1e12, "unit": "TOP/s",
                       "frac": eff_tops / (PEAK_INT8_OPS / 1e12)},

@@ -12,7 +12,8 @@ Public names mirror the C ABI in include/bpg.h:
     quantize_act_unrotated, w4a4_gemm_unrotated; and the expert layer's glue:
     moe_route_sort, w4a4_grouped_gemm_gather, swiglu_quantize_h32, moe_combine;
     and rotations over 64 or 128 values: rotate_pack_weights_rot,
-    quantize_act_rot, w4a4_gemm_rot
+    quantize_act_rot, w4a4_gemm_rot; and bf16 output: w4a4_gemm_bf16,
+    w4a4_grouped_gemm_bf16
 
 The binding is loaded lazily so that ``bit_prefill_gemm_amd.synth`` (input
 generators) imports without the HIP library.
@@ -24,6 +25,7 @@ _BINDING_NAMES = {
     "pack_weights_unrotated", "quantize_act_unrotated", "w4a4_gemm_unrotated",
     "moe_route_sort", "w4a4_grouped_gemm_gather", "swiglu_quantize_h32", "moe_combine",
     "rotate_pack_weights_rot", "quantize_act_rot", "w4a4_gemm_rot",
+    "w4a4_gemm_bf16", "w4a4_grouped_gemm_bf16",
 }
 
 

@@ -27,7 +27,8 @@ ENTRY_POINTS = ("bpg_status_str", "rotate_pack_weights_bytes", "rotate_pack_weig
                 "quantize_act_h32", "w4a4_gemm", "w4a4_grouped_gemm", "w4a4_gemm_blocksums",
                 "pack_weights_unrotated", "quantize_act_unrotated", "w4a4_gemm_unrotated",
                 "moe_route_sort", "w4a4_grouped_gemm_gather", "swiglu_quantize_h32", "moe_combine",
-                "rotate_pack_weights_rot", "quantize_act_rot", "w4a4_gemm_rot")
+                "rotate_pack_weights_rot", "quantize_act_rot", "w4a4_gemm_rot",
+                "w4a4_gemm_bf16", "w4a4_grouped_gemm_bf16")
 
 
 class WeightsDesc(ctypes.Structure):
@@ -70,14 +71,16 @@ def _lib_handle():
         fn = getattr(lib, name)
         fn.restype = ctypes.c_int
         fn.argtypes = [_vp, ctypes.c_int, _i64, _i64, _i64, ctypes.c_int, _vp, _vp, _vp]
-    for name in ("w4a4_gemm", "w4a4_gemm_unrotated"):
+    for name in ("w4a4_gemm", "w4a4_gemm_unrotated", "w4a4_gemm_bf16"):
         fn = getattr(lib, name)
         fn.restype = ctypes.c_int
         fn.argtypes = [_vp, _vp, ctypes.c_int, _i64, ctypes.POINTER(WeightsDesc), _vp, _vp,
                        _i64, _vp]
-    lib.w4a4_grouped_gemm.restype = ctypes.c_int
-    lib.w4a4_grouped_gemm.argtypes = [_vp, _vp, ctypes.c_int, _i64, _vp,
-                                      ctypes.POINTER(WeightsDesc), _vp, _vp, _i64, _vp]
+    for name in ("w4a4_grouped_gemm", "w4a4_grouped_gemm_bf16"):
+        fn = getattr(lib, name)
+        fn.restype = ctypes.c_int
+        fn.argtypes = [_vp, _vp, ctypes.c_int, _i64, _vp, ctypes.POINTER(WeightsDesc), _vp, _vp,
+                       _i64, _vp]
     lib.rotate_pack_weights_rot.restype = ctypes.c_int
     lib.rotate_pack_weights_rot.argtypes = [_vp, ctypes.c_int, _i64, _i64, _i64, ctypes.c_int, _vp,
                                             ctypes.c_size_t, ctypes.POINTER(WeightsDesc)]
@@ -219,11 +222,11 @@ def quantize_act_unrotated(x, act_bits: int = 4, codes=None, scales=None, stream
     return _quantize("quantize_act_unrotated", x, act_bits, codes, scales, stream)
 
 
-def _gemm(name: str, codes, scales, act_bits, w, y, stream):
+def _gemm(name: str, codes, scales, act_bits, w, y, stream, dtype=None):
     torch = _torch()
     m = codes.shape[0]
     if y is None:
-        y = torch.empty((m, w.n), dtype=torch.float32, device=codes.device)
+        y = torch.empty((m, w.n), dtype=dtype or torch.float32, device=codes.device)
     st = getattr(_lib_handle(), name)(_dptr(codes), _dptr(scales), act_bits, m,
                                       ctypes.byref(w.desc), _dptr(w.image), _dptr(y),
                                       y.stride(0), _stream_handle(stream))
@@ -235,23 +238,40 @@ def w4a4_gemm(codes, scales, act_bits: int, w: Weights, y=None, stream=None):
     return _gemm("w4a4_gemm", codes, scales, act_bits, w, y, stream)
 
 
+def w4a4_gemm_bf16(codes, scales, act_bits: int, w: Weights, y=None, stream=None):
+    """As w4a4_gemm with the result rounded to bf16 at the store (y: torch.bfloat16)."""
+    return _gemm("w4a4_gemm_bf16", codes, scales, act_bits, w, y, stream, _torch().bfloat16)
+
+
 def w4a4_gemm_unrotated(codes, scales, act_bits: int, w: Weights, y=None, stream=None):
     """The product of the unrotated route (image from pack_weights_unrotated)."""
     return _gemm("w4a4_gemm_unrotated", codes, scales, act_bits, w, y, stream)
 
 
-def w4a4_grouped_gemm(codes, scales, act_bits: int, expert_offsets, w: Weights, y=None,
-                      stream=None):
+def _grouped(name, codes, scales, act_bits, expert_offsets, w, y, stream, dtype):
     torch = _torch()
     rows = codes.shape[0]
     if y is None:
-        y = torch.empty((rows, w.n), dtype=torch.float32, device=codes.device)
-    st = _lib_handle().w4a4_grouped_gemm(_dptr(codes), _dptr(scales), act_bits, rows,
-                                         _dptr(expert_offsets), ctypes.byref(w.desc),
-                                         _dptr(w.image), _dptr(y), y.stride(0),
-                                         _stream_handle(stream))
-    _check(st, "w4a4_grouped_gemm")
+        y = torch.empty((rows, w.n), dtype=dtype, device=codes.device)
+    st = getattr(_lib_handle(), name)(_dptr(codes), _dptr(scales), act_bits, rows,
+                                      _dptr(expert_offsets), ctypes.byref(w.desc),
+                                      _dptr(w.image), _dptr(y), y.stride(0),
+                                      _stream_handle(stream))
+    _check(st, name)
     return y
+
+
+def w4a4_grouped_gemm(codes, scales, act_bits: int, expert_offsets, w: Weights, y=None,
+                      stream=None):
+    return _grouped("w4a4_grouped_gemm", codes, scales, act_bits, expert_offsets, w, y, stream,
+                    _torch().float32)
+
+
+def w4a4_grouped_gemm_bf16(codes, scales, act_bits: int, expert_offsets, w: Weights, y=None,
+                           stream=None):
+    """As w4a4_grouped_gemm with the result rounded to bf16 at the store."""
+    return _grouped("w4a4_grouped_gemm_bf16", codes, scales, act_bits, expert_offsets, w, y,
+                    stream, _torch().bfloat16)
 
 
 def w4a4_gemm_blocksums(codes, scales, act_bits: int, w: Weights, m0: int, m1: int, n0: int,

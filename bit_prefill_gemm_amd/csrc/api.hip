@@ -310,9 +310,10 @@ bpg_status quantize_checked(const void *x, bpg_x_dtype dt, int64_t m, int64_t k,
                                               scales, static_cast<hipStream_t>(stream)));
 }
 
+// y: fp32 [m][ldy], or bf16 bits when y_bf16 (rows 16-byte aligned either way)
 bpg_status gemm_checked(const void *codes, const float *scales, int act_bits, int64_t m,
-                        const bpg_weights_desc *w, const void *w_dev, float *y, int64_t ldy,
-                        void *stream, uint32_t rotation)
+                        const bpg_weights_desc *w, const void *w_dev, void *y, bool y_bf16,
+                        int64_t ldy, void *stream, uint32_t rotation)
 {
     if (!w)
         return BPG_ERR_NULL;
@@ -328,7 +329,7 @@ bpg_status gemm_checked(const void *codes, const float *scales, int act_bits, in
         return BPG_ERR_SHAPE;
     if (!w_dev || (m > 0 && !y))
         return BPG_ERR_NULL;
-    if (!aligned16(w_dev) || !aligned16(y) || ldy % 4 != 0)
+    if (!aligned16(w_dev) || !aligned16(y) || ldy % (y_bf16 ? 8 : 4) != 0)
         return BPG_ERR_ALIGN;
     s = check_device();
     if (s != BPG_OK)
@@ -343,7 +344,10 @@ bpg_status gemm_checked(const void *codes, const float *scales, int act_bits, in
     p.k = w->k;
     p.experts = 1;
     p.act_bits = act_bits;
-    p.y = y;
+    if (y_bf16)
+        p.y16 = static_cast<uint16_t *>(y);
+    else
+        p.y = static_cast<float *>(y);
     p.ldy = ldy;
     return launch_status(bpg::launch_gemm(p, static_cast<hipStream_t>(stream)));
 }
@@ -383,14 +387,21 @@ bpg_status w4a4_gemm(const void *codes, const float *scales, int act_bits, int64
                      const bpg_weights_desc *w, const void *w_dev, float *y, int64_t ldy,
                      void *stream)
 {
-    return gemm_checked(codes, scales, act_bits, m, w, w_dev, y, ldy, stream, 32);
+    return gemm_checked(codes, scales, act_bits, m, w, w_dev, y, false, ldy, stream, 32);
+}
+
+bpg_status w4a4_gemm_bf16(const void *codes, const float *scales, int act_bits, int64_t m,
+                          const bpg_weights_desc *w, const void *w_dev, uint16_t *y, int64_t ldy,
+                          void *stream)
+{
+    return gemm_checked(codes, scales, act_bits, m, w, w_dev, y, true, ldy, stream, 32);
 }
 
 bpg_status w4a4_gemm_unrotated(const void *codes, const float *scales, int act_bits, int64_t m,
                                const bpg_weights_desc *w, const void *w_dev, float *y,
                                int64_t ldy, void *stream)
 {
-    return gemm_checked(codes, scales, act_bits, m, w, w_dev, y, ldy, stream, 0);
+    return gemm_checked(codes, scales, act_bits, m, w, w_dev, y, false, ldy, stream, 0);
 }
 
 bpg_status rotate_pack_weights_rot(const void *src, bpg_src_kind kind, int64_t n, int64_t k,
@@ -416,7 +427,7 @@ bpg_status w4a4_gemm_rot(const void *codes, const float *scales, int act_bits, i
 {
     if (rotation != 32 && rotation != 64 && rotation != 128)
         return BPG_ERR_SHAPE;
-    return gemm_checked(codes, scales, act_bits, m, w, w_dev, y, ldy, stream, (uint32_t)rotation);
+    return gemm_checked(codes, scales, act_bits, m, w, w_dev, y, false, ldy, stream, (uint32_t)rotation);
 }
 
 } // extern "C"
@@ -427,7 +438,7 @@ namespace {
 bpg_status grouped_checked(const void *codes, const float *scales, int act_bits, bool gather,
                            int64_t src_rows, const int32_t *row_ids, int64_t total_rows,
                            const int32_t *expert_offsets_dev, const bpg_weights_desc *w,
-                           const void *w_dev, float *y, int64_t ldy, void *stream)
+                           const void *w_dev, void *y, bool y_bf16, int64_t ldy, void *stream)
 {
     if (!w)
         return BPG_ERR_NULL;
@@ -455,7 +466,7 @@ bpg_status grouped_checked(const void *codes, const float *scales, int act_bits,
         return BPG_ERR_SHAPE;
     if (!w_dev || !expert_offsets_dev || (total_rows > 0 && !y))
         return BPG_ERR_NULL;
-    if (!aligned16(w_dev) || !aligned16(y) || ldy % 4 != 0 ||
+    if (!aligned16(w_dev) || !aligned16(y) || ldy % (y_bf16 ? 8 : 4) != 0 ||
         (reinterpret_cast<uintptr_t>(expert_offsets_dev) & 3u) != 0 ||
         (reinterpret_cast<uintptr_t>(row_ids) & 3u) != 0)
         return BPG_ERR_ALIGN;
@@ -472,7 +483,10 @@ bpg_status grouped_checked(const void *codes, const float *scales, int act_bits,
     p.k = w->k;
     p.experts = w->num_experts;
     p.act_bits = act_bits;
-    p.y = y;
+    if (y_bf16)
+        p.y16 = static_cast<uint16_t *>(y);
+    else
+        p.y = static_cast<float *>(y);
     p.ldy = ldy;
     p.offsets = expert_offsets_dev;
     p.row_ids = gather ? row_ids : nullptr;
@@ -490,7 +504,16 @@ bpg_status w4a4_grouped_gemm(const void *codes, const float *scales, int act_bit
                              int64_t ldy, void *stream)
 {
     return grouped_checked(codes, scales, act_bits, false, total_rows, nullptr, total_rows,
-                           expert_offsets_dev, w, w_dev, y, ldy, stream);
+                           expert_offsets_dev, w, w_dev, y, false, ldy, stream);
+}
+
+bpg_status w4a4_grouped_gemm_bf16(const void *codes, const float *scales, int act_bits,
+                                  int64_t total_rows, const int32_t *expert_offsets_dev,
+                                  const bpg_weights_desc *w, const void *w_dev, uint16_t *y,
+                                  int64_t ldy, void *stream)
+{
+    return grouped_checked(codes, scales, act_bits, false, total_rows, nullptr, total_rows,
+                           expert_offsets_dev, w, w_dev, y, true, ldy, stream);
 }
 
 bpg_status w4a4_grouped_gemm_gather(const void *codes, const float *scales, int act_bits,
@@ -500,7 +523,7 @@ bpg_status w4a4_grouped_gemm_gather(const void *codes, const float *scales, int 
                                     int64_t ldy, void *stream)
 {
     return grouped_checked(codes, scales, act_bits, true, src_rows, row_ids_dev, total_rows,
-                           expert_offsets_dev, w, w_dev, y, ldy, stream);
+                           expert_offsets_dev, w, w_dev, y, false, ldy, stream);
 }
 
 bpg_status moe_route_sort(const int32_t *expert_of_dev, int64_t tokens, int64_t topk,

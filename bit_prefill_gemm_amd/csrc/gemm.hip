@@ -605,7 +605,7 @@ __global__ __launch_bounds__(C::kThreads, C::kOcc) void w4a4_kernel(GemmProblem 
                     v += red[(((grp * WK + w) * R + tt) * RG + r) * 64 + lane];
                 const int rl = M::out_row(g, r);
                 if (rl < vrows[i])
-                    p.y[(row0 + (wm * TM + i) * MF + rl) * p.ldy + col] = v * unscale;
+                    store_y(p, (row0 + (wm * TM + i) * MF + rl) * p.ldy + col, v * unscale);
             }
         }
         __syncthreads();

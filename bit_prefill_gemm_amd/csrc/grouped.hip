@@ -424,14 +424,14 @@ __global__ __launch_bounds__(256, 2) void grouped_kernel(GemmProblem p, int tile
     // the wave's 32x32 tile of 32 rows (rbase: 0 or 32) of an item; the
     // widening factor 256 is removed here; acc is cleared
     auto store = [&](float (&acc)[16], const Item &it, int rbase) __attribute__((always_inline)) {
-        float *y = p.y + ((int64_t)it.row0 + rbase + 4 * hk) * p.ldy +
-                   ((int64_t)it.ct * C::BN + wave * 32 + c);
+        const int64_t y0 = ((int64_t)it.row0 + rbase + 4 * hk) * p.ldy +
+                           ((int64_t)it.ct * C::BN + wave * 32 + c);
         const int lim = it.rows - rbase - 4 * hk;
 #pragma unroll
         for (int r = 0; r < 16; r++) {
             const int ro = 8 * (r >> 2) + (r & 3);
             if (ro < lim)
-                y[(int64_t)ro * p.ldy] = acc[r] * (1.0f / 256.0f);
+                store_y(p, y0 + (int64_t)ro * p.ldy, acc[r] * (1.0f / 256.0f));
             acc[r] = 0.0f;
         }
     };

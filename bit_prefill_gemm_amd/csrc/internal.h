@@ -33,8 +33,10 @@ struct GemmProblem {
     int64_t rows;            // activation rows
     int64_t n, k, experts;
     int act_bits;
-    // dense / grouped output
+    // dense / grouped output: fp32 y, or bf16 (round to nearest even) y16
+    // when y16 is set; [rows][ldy] elements
     float *y;
+    uint16_t *y16;
     int64_t ldy;
     const int32_t *offsets;  // grouped only: [experts+1] on the device
     // grouped only, optional: sorted row r reads activation row row_ids[r]

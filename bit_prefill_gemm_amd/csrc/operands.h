@@ -18,6 +18,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "internal.h"
+
 namespace bpg {
 namespace {
 
@@ -44,6 +46,23 @@ __device__ __forceinline__ long pack2(uint32_t lo, uint32_t hi)
 __device__ __forceinline__ float half_bits_to_float(uint16_t h)
 {
     return (float)__builtin_bit_cast(_Float16, h);
+}
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs)
+__device__ __forceinline__ uint16_t bf16_rne(float v)
+{
+    const uint32_t u = __float_as_uint(v);
+    return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+// One output element: fp32, or bf16 when the problem asks for it (the
+// choice is uniform across the launch).
+__device__ __forceinline__ void store_y(const GemmProblem &p, int64_t idx, float v)
+{
+    if (p.y16)
+        p.y16[idx] = bf16_rne(v);
+    else
+        p.y[idx] = v;
 }
 
 // Workgroups are dispatched round-robin over the 8 XCDs (w % 8 selects the

@@ -305,7 +305,7 @@ __global__ __launch_bounds__(C::kThreads) void skinny_kernel(GemmProblem p)
         const int i = q / (TN * 4), j = (q / 4) % TN, r = q % 4;
         const int m = 16 * i + 4 * (ln >> 4) + r;
         if (m < rows)
-            p.y[(int64_t)m * p.ldy + col0 + 16 * j + (ln & 15)] = s * unscale;
+            store_y(p, (int64_t)m * p.ldy + col0 + 16 * j + (ln & 15), s * unscale);
     }
 }
 

@@ -329,7 +329,7 @@ __global__ __launch_bounds__(512, 1) void wide_kernel(GemmProblem p, int tiles_m
                     v += red[((wm * 4 + w) * 16 + r) * 64 + lane];
                 const int rl = wm * 32 + M::out_row(hk, r);
                 if (rl < rows_valid)
-                    p.y[(row0 + rl) * p.ldy + col0 + (j0 + jj) * 32 + c] = v * (1.0f / 256.0f);
+                    store_y(p, (row0 + rl) * p.ldy + col0 + (j0 + jj) * 32 + c, v * (1.0f / 256.0f));
             }
         }
         if (j0 + 2 < TN)

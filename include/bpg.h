@@ -267,6 +267,27 @@ bpg_status w4a4_grouped_gemm(const void *codes, const float *scales, int act_bit
                              int64_t ldy, void *stream);
 
 /*
+ * bf16 output.  The pages accumulate the product in fp32 and say nothing of
+ * the type the result is stored in ("509 tokens a second of prompt: the
+ * Hadamard route ships", section "Why prompts are a matrix-unit problem");
+ * these variants compute exactly as w4a4_gemm / w4a4_grouped_gemm and round
+ * each fp32 result to bf16 (round to nearest even) at the store, halving the
+ * output bytes.  Every element equals bf16_rne of the fp32 variant's result.
+ *
+ *   y    device, [m or total_rows][ldy] bf16 (uint16 bit patterns),
+ *        ldy >= w->n, ldy % 8 == 0 (16-byte aligned rows); overwritten
+ *        (grouped: rows outside every expert's range untouched)
+ * Other arguments, limits and errors as w4a4_gemm / w4a4_grouped_gemm.
+ */
+bpg_status w4a4_gemm_bf16(const void *codes, const float *scales, int act_bits, int64_t m,
+                          const bpg_weights_desc *w, const void *w_dev, uint16_t *y,
+                          int64_t ldy, void *stream);
+bpg_status w4a4_grouped_gemm_bf16(const void *codes, const float *scales, int act_bits,
+                                  int64_t total_rows, const int32_t *expert_offsets_dev,
+                                  const bpg_weights_desc *w, const void *w_dev, uint16_t *y,
+                                  int64_t ldy, void *stream);
+
+/*
  * The expert layer around the grouped product ("Where the engine is going: HRX
  * and the NPU", section "4-bit activations reach the MoE experts": the route
  * covers the expert matmuls; the pages give no detail of the layer around

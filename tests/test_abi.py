@@ -328,3 +328,47 @@ def test_rotation_length_errors():
         assert g(128, dd) == DEVICE
         assert g(32, good_desc()) == DEVICE
         assert lib.quantize_act_rot(P, 0, 4, 256, 256, 4, 64, P2, P, NUL) == DEVICE
+
+
+def gemm_b(desc=None, **kw):
+    d = desc if desc is not None else good_desc()
+    a = dict(codes=P, scales=P2, bits=4, m=4, wdev=P, y=P2, ldy=64, stream=NUL)
+    a.update(kw)
+    return bb.lib().w4a4_gemm_bf16(a["codes"], a["scales"], a["bits"], a["m"], ctypes.byref(d),
+                                   a["wdev"], a["y"], a["ldy"], a["stream"])
+
+
+def grouped_b(desc=None, **kw):
+    d = desc if desc is not None else good_desc(e=3)
+    a = dict(codes=P, scales=P2, bits=4, rows=4, off=P, wdev=P, y=P2, ldy=64, stream=NUL)
+    a.update(kw)
+    return bb.lib().w4a4_grouped_gemm_bf16(a["codes"], a["scales"], a["bits"], a["rows"],
+                                           a["off"], ctypes.byref(d), a["wdev"], a["y"],
+                                           a["ldy"], a["stream"])
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(desc=_desc_with(magic=0)), STAMP), (dict(desc=good_desc(e=2)), STAMP),
+    (dict(bits=2), DTYPE), (dict(m=-3), SHAPE), (dict(ldy=32), SHAPE),
+    (dict(codes=NUL), NULL), (dict(y=NUL), NULL), (dict(y=MIS), ALIGN),
+    (dict(ldy=68), ALIGN),                           # bf16 rows: ldy % 8 (16-byte rows)
+])
+def test_gemm_bf16_errors(kwargs, status):
+    assert gemm_b(**kwargs) == status
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(off=NUL), NULL), (dict(y=MIS), ALIGN), (dict(ldy=68), ALIGN), (dict(bits=7), DTYPE),
+    (dict(rows=-1), SHAPE), (dict(ldy=16), SHAPE), (dict(desc=_desc_with(magic=1)), STAMP),
+])
+def test_grouped_bf16_errors(kwargs, status):
+    assert grouped_b(**kwargs) == status
+
+
+def test_bf16_ldy_multiple_of_8_passes_checks():
+    """A bf16 output with ldy a multiple of 8 (not of 16) passes every argument check; on a
+    host without a GPU the call then stops at the device check."""
+    if os.path.exists("/dev/kfd"):
+        pytest.skip("host has a GPU driver")
+    assert gemm_b(ldy=72) == DEVICE
+    assert grouped_b(ldy=72) == DEVICE
