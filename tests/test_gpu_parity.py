@@ -163,15 +163,17 @@ def test_gemm_ragged_shapes(torch, m, k, n, bits):
     check_gemm(case["x"], case["w"], n, k, bits, label="ragged")
 
 
+@pytest.mark.parametrize("bits", [4, 8])
 @pytest.mark.parametrize("m,k,n", [(200, 1056, 10240), (77, 544, 20480), (130, 96, 8192),
                                    (256, 2080, 10240), (64, 32, 40960)])
-def test_gemm_wide_tiles(torch, m, k, n):
-    """Shapes large enough in M x N for the 64 x 160 / 64 x 128 direct-load
-    kernel (4-bit): ragged last row tile, K with a partial last group and a
-    partial last stage, fewer groups than K waves (K = 96 and 32)."""
+def test_gemm_wide_tiles(torch, m, k, n, bits):
+    """Shapes large enough in M x N for the 64 x 160 / 64 x 128 tiles (4-bit:
+    the direct-load kernel; 8-bit: the tiled kernel): ragged last row tile, K
+    with a partial last group and a partial last stage, fewer groups than K
+    waves (K = 96 and 32)."""
     case = synth.small_dense(m, k, n, seed=m + 3 * k + n)
     rows = sample_rows(m, 10, seed=m + k)
-    check_gemm(case["x"], case["w"], n, k, 4, rows=rows, label="wide")
+    check_gemm(case["x"], case["w"], n, k, bits, rows=rows, label="wide")
 
 
 @pytest.mark.parametrize("m", [1, 7, 16, 17, 32])
