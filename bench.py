@@ -74,9 +74,11 @@ WORKLOADS = {
     # GEMM, SwiGLU-rotate-quantize, down GEMM, weighted combine
     "moe512_layer": dict(m=512, k=2048, n=2048, experts=128, tokens=512, layer=True),
 }
-# kernel sources of the GEMM paths (the tiled and grouped kernels, and the
-# weight-stream kernel used for a few rows)
-GEMM_SRCS = [os.path.join(ROOT, "bit_prefill_gemm_amd", "csrc", f) for f in ("gemm.hip", "skinny.hip", "wide.hip", "grouped.hip", "operands.h")]
+# kernel sources of the GEMM paths (the tiled, wide, strip and grouped kernels,
+# and the weight-stream kernel used for a few rows)
+GEMM_SRCS = [os.path.join(ROOT, "bit_prefill_gemm_amd", "csrc", f)
+             for f in ("gemm.hip", "skinny.hip", "wide.hip", "strip.hip", "grouped.hip",
+                       "operands.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_traffic.json")
 # timed steps between two whose GEMM is bracketed by events
 EVENT_EVERY = 8

@@ -15,7 +15,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libbpg.so")
-SOURCES = ["api.hip", "quantize.hip", "gemm.hip", "skinny.hip", "wide.hip", "grouped.hip", "moe.hip"]
+SOURCES = ["api.hip", "quantize.hip", "gemm.hip", "skinny.hip", "wide.hip", "strip.hip", "grouped.hip", "moe.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",

@@ -686,9 +686,15 @@ hipError_t launch_dense_bits(const GemmProblem &p, hipStream_t stream)
     for (int i = 0; i < 3; i++)
         if (e[i] < e[best])
             best = i;
-    // 4-bit activations: the wide shapes run the direct-load kernel (wide.hip)
-    if (BITS == 4 && best <= 1 && wide_fits(p, best == 0 ? 5 : 4))
-        return launch_wide(p, best == 0 ? 5 : 4, stream);
+    // 4-bit activations run the direct-load kernels: 64 x 160 tiles where
+    // they are the estimate's choice (wide.hip), else 32 x 128 strips
+    // (strip.hip), which measured as fast as or faster than the 64 x 128,
+    // 64 x 64 and 64 x 32 tiles on every shape tried (K = 2048 .. 5120,
+    // M = 128 .. 4096, N = 1536 .. 17408: up to 18% faster)
+    if (BITS == 4 && best == 0 && wide_fits(p))
+        return launch_wide(p, stream);
+    if (BITS == 4 && strip_fits(p))
+        return launch_strip(p, stream);
     switch (best) {
     case 0: return launch_dense_cfg<typename T::W64x160>(p, stream);
     case 1: return launch_dense_cfg<typename T::W64x128>(p, stream);

@@ -53,10 +53,14 @@ hipError_t launch_gemm(const GemmProblem &p, hipStream_t stream);
 // skinny_fits(p).
 bool skinny_fits(const GemmProblem &p);
 hipError_t launch_skinny(const GemmProblem &p, hipStream_t stream);
-// The wide-tile kernel (4-bit activations, dense, many rows): 64 x 32*tn
-// tiles, tn = 4 or 5; usable when wide_fits(p, tn).
-bool wide_fits(const GemmProblem &p, int tn);
-hipError_t launch_wide(const GemmProblem &p, int tn, hipStream_t stream);
+// The wide-tile kernel (4-bit activations, dense, many rows): 64 x 160
+// tiles; usable when wide_fits(p).
+bool wide_fits(const GemmProblem &p);
+hipError_t launch_wide(const GemmProblem &p, hipStream_t stream);
+// The strip kernel (4-bit activations, dense): 32 x 128 tiles, one 32-column
+// tile per wave over all of K; usable when strip_fits(p).
+bool strip_fits(const GemmProblem &p);
+hipError_t launch_strip(const GemmProblem &p, hipStream_t stream);
 // The grouped kernel on 64-row expert slots (4-bit activations, n a multiple
 // of 128, at most 1024 experts): usable when grouped_wide_fits(p).
 bool grouped_wide_fits(const GemmProblem &p);

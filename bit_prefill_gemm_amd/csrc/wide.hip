@@ -1,4 +1,4 @@
-// wide.hip -- the W4A4 product for many rows on 64 x 32*TN tiles (gfx950).
+// wide.hip -- the W4A4 product for many rows on 64 x 160 tiles (gfx950).
 //
 // "509 tokens a second of prompt: the Hadamard route ships", section "Why
 // prompts are a matrix-unit problem": with hundreds of rows the product is
@@ -350,15 +350,18 @@ hipError_t launch_tn(const GemmProblem &p, hipStream_t stream)
 
 } // namespace
 
-bool wide_fits(const GemmProblem &p, int tn)
+// 64 x 160 tiles (narrower tiles of this kernel lose to the strip kernel)
+constexpr int kWideTN = 5;
+
+bool wide_fits(const GemmProblem &p)
 {
-    return p.act_bits == 4 && p.experts == 1 && (tn == 4 || tn == 5) && p.n % (32 * tn) == 0 &&
-           p.rows > 0 && (p.rows + 63) / 64 * (p.n / (32 * tn)) < (int64_t)1 << 31;
+    return p.act_bits == 4 && p.experts == 1 && p.n % (32 * kWideTN) == 0 && p.rows > 0 &&
+           (p.rows + 63) / 64 * (p.n / (32 * kWideTN)) < (int64_t)1 << 31;
 }
 
-hipError_t launch_wide(const GemmProblem &p, int tn, hipStream_t stream)
+hipError_t launch_wide(const GemmProblem &p, hipStream_t stream)
 {
-    return tn == 5 ? launch_tn<5>(p, stream) : launch_tn<4>(p, stream);
+    return launch_tn<kWideTN>(p, stream);
 }
 
 } // namespace bpg

@@ -1,6 +1,6 @@
 """GPU parity of the bf16-output variants: every element equals the fp32
 variant's result rounded to bf16 (round to nearest even), bit for bit, on each
-kernel family (wide 4-bit tiles, tiled 8-bit, the weight-stream kernel for a
+kernel family (wide 4-bit tiles, the strip kernel, tiled 8-bit, the weight-stream kernel for a
 few rows, the expert-slot kernel, the tiled grouped kernel); the bf16 result
 is also within bf16 rounding of the oracle; grouped rows outside every
 expert's range stay untouched.
@@ -37,8 +37,9 @@ def quantized(x, bits):
 
 
 @pytest.mark.parametrize("m,k,n,bits", [
-    (200, 1056, 1280, 4),    # wide kernel, 64x160 tiles, ragged rows
-    (130, 512, 1024, 4),     # wide kernel, 64x128 tiles
+    (200, 1056, 10240, 4),   # wide kernel, 64x160 tiles, ragged rows
+    (130, 512, 1024, 4),     # strip kernel
+    (1000, 448, 12288, 4),   # strip kernel, ragged last strip
     (77, 320, 96, 8),        # tiled kernel, 8-bit
     (16, 2048, 512, 4),      # weight-stream kernel
     (5, 96, 64, 8),          # weight-stream kernel, 8-bit, tiny

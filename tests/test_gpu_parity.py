@@ -167,13 +167,27 @@ def test_gemm_ragged_shapes(torch, m, k, n, bits):
 @pytest.mark.parametrize("m,k,n", [(200, 1056, 10240), (77, 544, 20480), (130, 96, 8192),
                                    (256, 2080, 10240), (64, 32, 40960)])
 def test_gemm_wide_tiles(torch, m, k, n, bits):
-    """Shapes large enough in M x N for the 64 x 160 / 64 x 128 tiles (4-bit:
-    the direct-load kernel; 8-bit: the tiled kernel): ragged last row tile, K
-    with a partial last group and a partial last stage, fewer groups than K
-    waves (K = 96 and 32)."""
+    """Shapes large enough in M x N for the wide tiles (4-bit: the 64 x 160
+    direct-load kernel, or the strip kernel where N = 8192 is not a multiple
+    of 160; 8-bit: the tiled kernel): ragged last row tile, K with a partial
+    last group and a partial last stage, fewer groups than K waves (K = 96
+    and 32)."""
     case = synth.small_dense(m, k, n, seed=m + 3 * k + n)
     rows = sample_rows(m, 10, seed=m + k)
     check_gemm(case["x"], case["w"], n, k, bits, rows=rows, label="wide")
+
+
+@pytest.mark.parametrize("m,k,n", [(1000, 1056, 12288), (1000, 448, 12288), (2048, 160, 6144),
+                                   (4096, 96, 17408)])
+def test_gemm_strip_tiles(torch, m, k, n):
+    """4-bit shapes with N a multiple of 128 but not of 160 and at least 3072
+    strips of 32 x 128, which run the strip kernel (one 32-column tile per
+    wave over all of K): ragged last strip (M = 1000), K with an odd number of
+    4-block groups and a one-block last stage (1056), an even number with a
+    partial last group (448), one stage (160) and one partial group (96)."""
+    case = synth.small_dense(m, k, n, seed=m + 5 * k + n)
+    rows = sample_rows(m, 24, seed=m + k + 1)
+    check_gemm(case["x"], case["w"], n, k, 4, rows=rows, label="strip")
 
 
 @pytest.mark.parametrize("m", [1, 7, 16, 17, 32])
