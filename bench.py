@@ -61,6 +61,10 @@ PEAK_FP32_FLOPS = 157.3e12
 WORKLOADS = {
     "attn512": dict(m=512, k=5120, n=5120),
     "long1024": dict(m=1024, k=5120, n=17408),
+    # the dense FFN pair (Student-t activations): gate (up is the same shape)
+    # and down projections
+    "ffn512_gate": dict(m=512, k=5120, n=17408, src="ffn512", x="x1", w="w_gate"),
+    "ffn512_down": dict(m=512, k=17408, n=5120, src="ffn512", x="x2", w="w_down"),
     "m16_gate": dict(m=16, k=5120, n=17408),
     "m16_down": dict(m=16, k=17408, n=5120),
     "m16_attn": dict(m=16, k=5120, n=5120),
