@@ -178,13 +178,16 @@ def test_gemm_wide_tiles(torch, m, k, n, bits):
 
 
 @pytest.mark.parametrize("m,k,n", [(1000, 1056, 12288), (1000, 448, 12288), (2048, 160, 6144),
-                                   (4096, 96, 17408)])
+                                   (4096, 96, 17408), (1024, 32, 12288), (33, 32, 128),
+                                   (40, 1056, 256), (65, 640, 640)])
 def test_gemm_strip_tiles(torch, m, k, n):
-    """4-bit shapes with N a multiple of 128 but not of 160 and at least 3072
-    strips of 32 x 128, which run the strip kernel (one 32-column tile per
-    wave over all of K): ragged last strip (M = 1000), K with an odd number of
-    4-block groups and a one-block last stage (1056), an even number with a
-    partial last group (448), one stage (160) and one partial group (96)."""
+    """4-bit shapes with more than 32 rows, N a multiple of 128 and 64 x 160
+    tiles not the estimator's choice, which run the strip kernel (one
+    32-column tile per wave over all of K): ragged last strip (M = 1000, and
+    a last strip of one row: M = 33, 65), K with an odd number of 4-block
+    groups and a one-block last stage (1056), an even number with a partial
+    last group (448), one stage (160), one partial group (96) and a single
+    block (32); a few workgroups (M = 33, N = 128) up to thousands."""
     case = synth.small_dense(m, k, n, seed=m + 5 * k + n)
     rows = sample_rows(m, 24, seed=m + k + 1)
     check_gemm(case["x"], case["w"], n, k, 4, rows=rows, label="strip")
