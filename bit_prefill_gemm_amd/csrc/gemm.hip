@@ -690,10 +690,15 @@ hipError_t launch_dense_bits(const GemmProblem &p, hipStream_t stream)
     // they are the estimate's choice (wide.hip), else 32 x 128 strips
     // (strip.hip), which measured as fast as or faster than the 64 x 128,
     // 64 x 64 and 64 x 32 tiles on every shape tried (K = 2048 .. 5120,
-    // M = 128 .. 4096, N = 1536 .. 17408: up to 18% faster)
+    // M = 128 .. 4096, N = 1536 .. 17408: up to 18% faster).  8-bit codes
+    // run the strip kernel too (up to 33% faster than the tiled kernel),
+    // except where the estimate picks 64 x 160 tiles and there are fewer
+    // strips than three per CU: there the tiled kernel's K-split workgroups
+    // fill every CU and the strips do not (M = 512, K = 17408, N = 5120).
     if (BITS == 4 && best == 0 && wide_fits(p))
         return launch_wide(p, stream);
-    if (BITS == 4 && strip_fits(p))
+    if (strip_fits(p) &&
+        (BITS == 4 || best != 0 || (p.rows + 31) / 32 * (p.n / 128) >= 3 * kCUs))
         return launch_strip(p, stream);
     switch (best) {
     case 0: return launch_dense_cfg<typename T::W64x160>(p, stream);

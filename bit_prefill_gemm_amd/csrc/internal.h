@@ -57,8 +57,8 @@ hipError_t launch_skinny(const GemmProblem &p, hipStream_t stream);
 // tiles; usable when wide_fits(p).
 bool wide_fits(const GemmProblem &p);
 hipError_t launch_wide(const GemmProblem &p, hipStream_t stream);
-// The strip kernel (4-bit activations, dense): 32 x 128 tiles, one 32-column
-// tile per wave over all of K; usable when strip_fits(p).
+// The strip kernel (4- or 8-bit activations, dense): 32 x 128 tiles, one
+// 32-column tile per wave over all of K; usable when strip_fits(p).
 bool strip_fits(const GemmProblem &p);
 hipError_t launch_strip(const GemmProblem &p, hipStream_t stream);
 // The grouped kernel on 64-row expert slots (4-bit activations, n a multiple

@@ -33,33 +33,43 @@ namespace bpg {
 
 namespace {
 
+template <int BITS_>
 struct StripCfg {
+    static constexpr int BITS = BITS_;              // activation code width
     static constexpr int TN = 4;                    // waves = 32-column tiles
     static constexpr int BM = 32, BN = 32 * TN;
     static constexpr int kThreads = 64 * TN;
     static constexpr int kOcc = 3;                  // workgroups per CU
     static constexpr int kWavesPerSimd = 3;         // (kOcc * 4 waves over 4 SIMDs)
     static constexpr int kGroupBytes = 2304;        // image block: 32 columns x 4 K-blocks
-    static constexpr int kSB = 8;                   // blocks per stage (two groups)
-    static constexpr int kWTile = 2 * kGroupBytes;  // one tile's two groups of a stage
+    static constexpr int kAB = BITS == 4 ? 16 : 32; // code bytes per row and block
+    // blocks per stage: two groups for 4-bit codes, one for 8-bit (whose codes
+    // take twice the bytes: three double-buffered workgroups must fit the LDS)
+    static constexpr int kSB = BITS == 4 ? 8 : 4;
+    static constexpr int kGroups = kSB / 4;
+    static constexpr int kWTile = kGroups * kGroupBytes; // one tile's groups of a stage
     // one stage in LDS: image blocks [tile][group] verbatim, codes [row][8
-    // blocks] (16-byte blocks XOR-swizzled by row & 7), row scales [block][row]
+    // 16-byte chunks] (chunks XOR-swizzled by row & 7), row scales [block][row]
     static constexpr int kW = TN * kWTile;
-    static constexpr int kA = BM * kSB * 16;
+    static constexpr int kA = BM * kSB * kAB;
     static constexpr int kDa = kSB * BM * 4;
     static constexpr int kBuf = kW + kA + kDa;
     static constexpr int kWLoads = kW / 1024;       // wave-wide 16-byte weight loads
     static constexpr int kWPerWave = (kWLoads + TN - 1) / TN; // the last by some waves only
+    static constexpr int kDaWaves = kDa / 256;      // waves with a row-scale load
+    static constexpr float kUnscale = BITS == 4 ? 1.0f / 256.0f : 1.0f / 16.0f;
     static_assert(kW % 1024 == 0, "whole wave-wide weight loads");
-    static_assert(kA == 4 * 1024 && kDa == 4 * 256, "one code and one scale load per wave");
+    static_assert(kA == 4 * 1024 && kSB * kAB == 128, "one code load per wave, 128-byte rows");
+    static_assert(kDa % 256 == 0 && kDaWaves <= TN, "row-scale loads");
     static_assert(kOcc * 2 * kBuf <= 160 * 1024, "LDS budget");
 };
 
 // (the second bound is the minimum number of waves per SIMD)
-__global__ __launch_bounds__(StripCfg::kThreads, StripCfg::kWavesPerSimd) void strip_kernel(
-    GemmProblem p, int tiles_m)
+template <int BITS>
+__global__ __launch_bounds__(StripCfg<BITS>::kThreads, StripCfg<BITS>::kWavesPerSimd) void
+strip_kernel(GemmProblem p, int tiles_m)
 {
-    typedef StripCfg C;
+    typedef StripCfg<BITS> C;
     constexpr int TN = C::TN;
     typedef Mfma<32> M;
     typedef M::Op Op;
@@ -68,6 +78,7 @@ __global__ __launch_bounds__(StripCfg::kThreads, StripCfg::kWavesPerSimd) void s
     // loads into one from the reads of the other by the array they address)
     __shared__ __attribute__((aligned(16))) uint8_t buf0[C::kBuf];
     __shared__ __attribute__((aligned(16))) uint8_t buf1[C::kBuf];
+    constexpr int kG = C::kGroups;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -77,8 +88,8 @@ __global__ __launch_bounds__(StripCfg::kThreads, StripCfg::kWavesPerSimd) void s
 
     const int B = (int)(p.k / 32); // the host limits K to 2^22
     const int NG = (B + 3) / 4;
-    const int nst = (NG + 1) / 2;  // stages of two groups
-    const int64_t arow = p.k / 2;
+    const int nst = (NG + kG - 1) / kG; // stages of kG groups
+    const int64_t arow = p.k / 32 * C::kAB;
 
     const int L = xcd_remap(blockIdx.x, gridDim.x);
     const int64_t row0 = (int64_t)(L % tiles_m) * C::BM;
@@ -106,25 +117,26 @@ __global__ __launch_bounds__(StripCfg::kThreads, StripCfg::kWavesPerSimd) void s
         wgg |= (uint32_t)gg << u;
     }
     // codes: wave w loads chunks 64 w + lane = (row 8 w + lane / 8, slot
-    // lane % 8), slot j holding block j ^ (row & 7)
+    // lane % 8), slot j holding chunk j ^ (row & 7) of the row's 128 bytes
     const int arow_l = 8 * wave + (lane >> 3);
-    const int ablk = (lane & 7) ^ (arow_l & 7);
+    const int achunk = (lane & 7) ^ (arow_l & 7);
+    const int ablk = achunk / (C::kAB / 16);
     const uint32_t aoff =
-        (uint32_t)((arow_l < last_row ? arow_l : last_row) * arow + ablk * 16);
+        (uint32_t)((arow_l < last_row ? arow_l : last_row) * arow + achunk * 16);
     // row scales: wave w loads blocks 2w, 2w+1 (lane / 32) of rows lane % 32
     const uint32_t daoff =
         (uint32_t)(((c < last_row ? c : last_row) * B + hk) * 4);
 
     auto issue = [&](uint8_t *buf, int st) __attribute__((always_inline)) {
-        const int g0 = 2 * st;
+        const int g0 = kG * st;
         const uint8_t *wst = uniform(w_base + (size_t)g0 * C::kGroupBytes);
-        const uint8_t *ast = uniform(a_base + (size_t)st * (C::kSB * 16));
+        const uint8_t *ast = uniform(a_base + (size_t)st * (C::kSB * C::kAB));
         const uint8_t *dst = uniform(reinterpret_cast<const uint8_t *>(da_base + C::kSB * st));
         uint8_t *wl = buf;
         uint8_t *al = buf + C::kW;
         uint8_t *dl = buf + C::kW + C::kA;
         const bool tail = C::kSB * (st + 1) > B;
-        const bool over_g = g0 + 1 >= NG; // the stage's second group is past the image
+        const bool over_g = kG == 2 && g0 + 1 >= NG; // the stage's second group is past the image
 #pragma unroll
         for (int u = 0; u < C::kWPerWave; u++) {
             const int i = wave + TN * u;
@@ -143,9 +155,12 @@ __global__ __launch_bounds__(StripCfg::kThreads, StripCfg::kWavesPerSimd) void s
         else
             *reinterpret_cast<uint4 *>(adst + 16 * lane) = make_uint4(0u, 0u, 0u, 0u);
         // blocks 2 wave + hk of the stage; past K, block B-1
-        const int blk = C::kSB * st + 2 * wave + hk < B ? 2 * wave : B - 1 - C::kSB * st - hk;
-        __builtin_amdgcn_global_load_lds((glb_void *)(dst + opaque(daoff + 4 * blk)),
-                                         (lds_void *)(dl + 256 * wave), 4, 0, 0);
+        if (wave < C::kDaWaves) {
+            const int blk =
+                C::kSB * st + 2 * wave + hk < B ? 2 * wave : B - 1 - C::kSB * st - hk;
+            __builtin_amdgcn_global_load_lds((glb_void *)(dst + opaque(daoff + 4 * blk)),
+                                             (lds_void *)(dl + 256 * wave), 4, 0, 0);
+        }
     };
 
     float acc[16];
@@ -161,9 +176,12 @@ __global__ __launch_bounds__(StripCfg::kThreads, StripCfg::kWavesPerSimd) void s
     // one integer offset: longer address chains lose the array's identity,
     // and the compiler then waits for the direct loads into the other buffer
     // before the read).  Weight slots 2hk, 2hk+1 of the lane's column and its
-    // fp16 scales in group g of the wave's tile (+ 2304 g); codes of row c,
-    // bytes 8hk..8hk+7 (block q at slot q ^ (c & 7)); row scales of the
-    // lane's result rows 4hk + 8 r4 .. + 3 of block q (+ 128 q).
+    // fp16 scales in group g of the wave's tile (+ 2304 g); codes of row c:
+    // 4-bit, bytes 8hk..8hk+7 of block q (slot q ^ (c & 7)), 8-bit, bytes
+    // 8hk..8hk+7 of each 16-byte half of block q (slots 2q ^ (c & 7) and
+    // (2q + 1) ^ (c & 7)): the K values 8hk..8hk+7 and 16+8hk..16+8hk+7 that
+    // the weight operand holds; row scales of the lane's result rows
+    // 4hk + 8 r4 .. + 3 of block q (+ 128 q).
     const uint32_t w_rd = opaque((uint32_t)(wave * C::kWTile + ((2 * hk) * 32 + c) * 16));
     const uint32_t hw_rd =
         opaque((uint32_t)(wave * C::kWTile + 2048 + ((c & 15) * 2 + (c >> 4)) * 8));
@@ -175,23 +193,34 @@ __global__ __launch_bounds__(StripCfg::kThreads, StripCfg::kWavesPerSimd) void s
     // right after its matrix instruction: the other waves of the SIMD hide the
     // instruction's latency)
     auto compute = [&](const uint8_t *buf) __attribute__((always_inline)) {
-        uint4 wr[2][2];
-        uint2 hw[2];
+        uint4 wr[kG][2];
+        uint2 hw[kG];
 #pragma unroll
-        for (int g = 0; g < 2; g++) {
+        for (int g = 0; g < kG; g++) {
             wr[g][0] = *reinterpret_cast<const uint4 *>(buf + (w_rd + g * C::kGroupBytes));
             wr[g][1] = *reinterpret_cast<const uint4 *>(buf + (w_rd + g * C::kGroupBytes + 512));
             hw[g] = *reinterpret_cast<const uint2 *>(buf + (hw_rd + g * C::kGroupBytes));
         }
 #pragma unroll
         for (int q = 0; q < C::kSB; q++) {
-            const uint2 ad = *reinterpret_cast<const uint2 *>(
-                buf + (a_rd + (uint32_t)((q ^ csw) * 16)));
             Op a;
-            a[0] = (int)act_lo(ad.x);
-            a[1] = (int)act_lo(ad.y);
-            a[2] = (int)act_hi(ad.x);
-            a[3] = (int)act_hi(ad.y);
+            if (BITS == 4) {
+                const uint2 ad = *reinterpret_cast<const uint2 *>(
+                    buf + (a_rd + (uint32_t)((q ^ csw) * 16)));
+                a[0] = (int)act_lo(ad.x);
+                a[1] = (int)act_lo(ad.y);
+                a[2] = (int)act_hi(ad.x);
+                a[3] = (int)act_hi(ad.y);
+            } else {
+                const uint2 lo = *reinterpret_cast<const uint2 *>(
+                    buf + (a_rd + (uint32_t)(((2 * q) ^ csw) * 16)));
+                const uint2 hi = *reinterpret_cast<const uint2 *>(
+                    buf + (a_rd + (uint32_t)(((2 * q + 1) ^ csw) * 16)));
+                a[0] = (int)lo.x;
+                a[1] = (int)lo.y;
+                a[2] = (int)hi.x;
+                a[3] = (int)hi.y;
+            }
             float4 da[4];
 #pragma unroll
             for (int r4 = 0; r4 < 4; r4++)
@@ -247,14 +276,14 @@ __global__ __launch_bounds__(StripCfg::kThreads, StripCfg::kWavesPerSimd) void s
         }
     }
 
-    // the wave's tile; the widening factor 256 is removed here
+    // the wave's tile; the widening factor (256, 8-bit codes 16) is removed here
     const int64_t y0 = (row0 + 4 * hk) * p.ldy + col0 + wave * 32 + c;
     const int lim = last_row + 1 - 4 * hk; // rows of this lane's group that hold data
 #pragma unroll
     for (int r = 0; r < 16; r++) {
         const int ro = 8 * (r >> 2) + (r & 3);
         if (ro < lim)
-            store_y(p, y0 + (int64_t)ro * p.ldy, acc[r] * (1.0f / 256.0f));
+            store_y(p, y0 + (int64_t)ro * p.ldy, acc[r] * C::kUnscale);
     }
 }
 
@@ -262,17 +291,20 @@ __global__ __launch_bounds__(StripCfg::kThreads, StripCfg::kWavesPerSimd) void s
 
 bool strip_fits(const GemmProblem &p)
 {
-    return p.act_bits == 4 && p.experts == 1 && p.n % StripCfg::BN == 0 && p.rows > 0 &&
-           (p.rows + 31) / 32 * (p.n / StripCfg::BN) < (int64_t)1 << 31;
+    return (p.act_bits == 4 || p.act_bits == 8) && p.experts == 1 && p.n % 128 == 0 &&
+           p.rows > 0 && (p.rows + 31) / 32 * (p.n / 128) < (int64_t)1 << 31;
 }
 
 hipError_t launch_strip(const GemmProblem &p, hipStream_t stream)
 {
-    const int tm = (int)((p.rows + 31) / 32), tn = (int)(p.n / StripCfg::BN);
+    const int tm = (int)((p.rows + 31) / 32), tn = (int)(p.n / 128);
     const int64_t grid = (int64_t)tm * tn;
     if (grid <= 0)
         return hipSuccess;
-    strip_kernel<<<dim3((unsigned)grid), StripCfg::kThreads, 0, stream>>>(p, tm);
+    if (p.act_bits == 4)
+        strip_kernel<4><<<dim3((unsigned)grid), StripCfg<4>::kThreads, 0, stream>>>(p, tm);
+    else
+        strip_kernel<8><<<dim3((unsigned)grid), StripCfg<8>::kThreads, 0, stream>>>(p, tm);
     return hipGetLastError();
 }
 

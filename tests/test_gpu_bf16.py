@@ -40,6 +40,7 @@ def quantized(x, bits):
     (200, 1056, 10240, 4),   # wide kernel, 64x160 tiles, ragged rows
     (130, 512, 1024, 4),     # strip kernel
     (1000, 448, 12288, 4),   # strip kernel, ragged last strip
+    (130, 1056, 1024, 8),    # strip kernel, 8-bit
     (77, 320, 96, 8),        # tiled kernel, 8-bit
     (16, 2048, 512, 4),      # weight-stream kernel
     (5, 96, 64, 8),          # weight-stream kernel, 8-bit, tiny

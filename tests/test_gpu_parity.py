@@ -168,10 +168,10 @@ def test_gemm_ragged_shapes(torch, m, k, n, bits):
                                    (256, 2080, 10240), (64, 32, 40960)])
 def test_gemm_wide_tiles(torch, m, k, n, bits):
     """Shapes large enough in M x N for the wide tiles (4-bit: the 64 x 160
-    direct-load kernel, or the strip kernel where N = 8192 is not a multiple
-    of 160; 8-bit: the tiled kernel): ragged last row tile, K with a partial
-    last group and a partial last stage, fewer groups than K waves (K = 96
-    and 32)."""
+    direct-load kernel; 8-bit: the tiled kernel's 64 x 160 tiles; both the
+    strip kernel where N = 8192 is not a multiple of 160): ragged last row
+    tile, K with a partial last group and a partial last stage, fewer groups
+    than K waves (K = 96 and 32)."""
     case = synth.small_dense(m, k, n, seed=m + 3 * k + n)
     rows = sample_rows(m, 10, seed=m + k)
     check_gemm(case["x"], case["w"], n, k, bits, rows=rows, label="wide")
@@ -180,17 +180,19 @@ def test_gemm_wide_tiles(torch, m, k, n, bits):
 @pytest.mark.parametrize("m,k,n", [(1000, 1056, 12288), (1000, 448, 12288), (2048, 160, 6144),
                                    (4096, 96, 17408), (1024, 32, 12288), (33, 32, 128),
                                    (40, 1056, 256), (65, 640, 640)])
-def test_gemm_strip_tiles(torch, m, k, n):
+@pytest.mark.parametrize("bits", [4, 8])
+def test_gemm_strip_tiles(torch, m, k, n, bits):
     """4-bit shapes with more than 32 rows, N a multiple of 128 and 64 x 160
     tiles not the estimator's choice, which run the strip kernel (one
     32-column tile per wave over all of K): ragged last strip (M = 1000, and
     a last strip of one row: M = 33, 65), K with an odd number of 4-block
     groups and a one-block last stage (1056), an even number with a partial
     last group (448), one stage (160), one partial group (96) and a single
-    block (32); a few workgroups (M = 33, N = 128) up to thousands."""
+    block (32); a few workgroups (M = 33, N = 128) up to thousands.  8-bit
+    codes take stages of four blocks (one group) instead of eight."""
     case = synth.small_dense(m, k, n, seed=m + 5 * k + n)
     rows = sample_rows(m, 24, seed=m + k + 1)
-    check_gemm(case["x"], case["w"], n, k, 4, rows=rows, label="strip")
+    check_gemm(case["x"], case["w"], n, k, bits, rows=rows, label="strip")
 
 
 @pytest.mark.parametrize("m", [1, 7, 16, 17, 32])
