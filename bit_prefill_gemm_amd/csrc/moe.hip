@@ -41,53 +41,63 @@ __device__ __forceinline__ int block_scan_incl(int v, int *wsum)
     return before + incl;
 }
 
-// Counting sort with one workgroup per expert x.  Every workgroup counts the
-// entries of every expert (LDS atomics: the totals do not depend on their
-// order) to find x's offset; thread t owns the contiguous entry range
-// [t*per, (t+1)*per), counts its entries of expert x, and a scan over the
-// threads in order gives each such entry its place: the stable order.
-// Expert ids outside [0, experts) are clamped (the rows stay in bounds).
+// Counting sort with one workgroup per expert x.  Thread t owns the
+// contiguous entry range [t*per, (t+1)*per) and counts its entries of experts
+// before x and of x itself; the sum of the first counts over the workgroup is
+// x's offset, and a scan of the second over the threads in order gives each
+// entry of x its place: the stable order.  Expert ids outside [0, experts)
+// are clamped (the rows stay in bounds).
 __global__ __launch_bounds__(kSortThreads) void route_sort_kernel(
     const int32_t *__restrict__ expert_of, int n, int topk, int experts,
     int32_t *__restrict__ offsets, int32_t *__restrict__ row_token, int32_t *__restrict__ slot_of)
 {
-    extern __shared__ int32_t hist[]; // [experts], then kSortThreads / 64 ints
-    int *wsum = hist + experts;
+    __shared__ int wsum[kSortThreads / 64];
+    __shared__ int off_sh;
     const int x = blockIdx.x, tid = threadIdx.x;
     const int per = (n + kSortThreads - 1) / kSortThreads;
-    const int lo = tid * per, hi = lo + per < n ? lo + per : n;
+    const int lo = tid * per < n ? tid * per : n;
+    const int hi = lo + per < n ? lo + per : n;
     auto expert_at = [&](int i) {
         const int e = expert_of[i];
         return e < 0 ? 0 : (e >= experts ? experts - 1 : e);
     };
-
-    for (int e = tid; e < experts; e += kSortThreads)
-        hist[e] = 0;
-    __syncthreads();
-    int mine = 0; // entries of expert x in this thread's range
-    for (int i = lo; i < hi; i++) {
-        const int e = expert_at(i);
-        atomicAdd(&hist[e], 1);
+    // 16-byte loads where the range and the pointer allow them
+    const bool vec = per % 4 == 0 && (reinterpret_cast<uintptr_t>(expert_of) & 15) == 0;
+    int before = 0, mine = 0; // entries of experts below x, and of x
+    auto count = [&](int e) {
+        before += e < x;
         mine += e == x;
+    };
+    if (vec) {
+        for (int i = lo; i + 4 <= hi; i += 4) {
+            const int4 v = *reinterpret_cast<const int4 *>(expert_of + i);
+            const int ev[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int j = 0; j < 4; j++)
+                count(ev[j] < 0 ? 0 : (ev[j] >= experts ? experts - 1 : ev[j]));
+        }
+        for (int i = lo + (hi - lo) / 4 * 4; i < hi; i++)
+            count(expert_at(i));
+    } else {
+        for (int i = lo; i < hi; i++)
+            count(expert_at(i));
     }
-    __syncthreads();
     // offset of x: the entries of the experts before it
-    int part = 0;
-    for (int e = tid; e < x; e += kSortThreads)
-        part += hist[e];
-    const int offset = block_scan_incl(part, wsum);
-    __shared__ int off_sh;
+    const int offset = block_scan_incl(before, wsum);
     if (tid == kSortThreads - 1)
         off_sh = offset;
     __syncthreads();
     const int base_x = off_sh;
+    // places of this thread's entries of expert x
+    const int incl = block_scan_incl(mine, wsum);
     if (tid == 0) {
         offsets[x] = base_x;
         if (x == experts - 1)
-            offsets[experts] = base_x + hist[x];
+            offsets[experts] = n; // every entry's (clamped) expert is at most x
     }
-    // places of this thread's entries of expert x
-    int pos = base_x + block_scan_incl(mine, wsum) - mine;
+    if (mine == 0)
+        return;
+    int pos = base_x + incl - mine;
     for (int i = lo; i < hi; i++)
         if (expert_at(i) == x) {
             slot_of[i] = pos;
@@ -128,8 +138,7 @@ hipError_t launch_route_sort(const int32_t *expert_of, int64_t tokens, int64_t t
                              int64_t experts, int32_t *offsets, int32_t *row_token,
                              int32_t *slot_of, hipStream_t stream)
 {
-    const size_t lds = ((size_t)experts + kSortThreads / 64) * sizeof(int32_t);
-    route_sort_kernel<<<dim3((unsigned)experts), kSortThreads, lds, stream>>>(
+    route_sort_kernel<<<dim3((unsigned)experts), kSortThreads, 0, stream>>>(
         expert_of, (int)(tokens * topk), (int)topk, (int)experts, offsets, row_token, slot_of);
     return hipGetLastError();
 }
