@@ -254,6 +254,30 @@ def test_gemm_output_stride(torch):
     assert row_rel_err(yb[:, 4:68], ref) <= TIGHT
 
 
+@pytest.mark.parametrize("m,k,n,bits", [(200, 1056, 10240, 4),   # wide kernel
+                                        (200, 1056, 10240, 8),   # tiled 64 x 160
+                                        (96, 256, 640, 4),       # strip kernel
+                                        (1000, 160, 12288, 8)])  # strip kernel, 8-bit
+def test_gemm_output_stride_wide_shapes(torch, m, k, n, bits):
+    """A row stride larger than N (the output a column slice of a wider
+    matrix) on the kernels for many rows: columns outside the slice stay
+    untouched."""
+    case = synth.small_dense(m, k, n, seed=m + k + n + bits)
+    codes, scales, q, d = quantize_and_check(case["x"], bits)
+    W = weights_to_device(case["w"], n, k)
+    ybig = torch.full((m, n + 40), -1.0, device="cuda")
+    y = ybig[:, 8:8 + n]
+    print("gemm stride", m, k, n, bits, flush=True)
+    bb.w4a4_gemm(codes, scales, bits, W, y=y)
+    torch.cuda.synchronize()
+    yb = ybig.cpu().numpy()
+    assert np.all(yb[:, :8] == -1.0) and np.all(yb[:, 8 + n:] == -1.0)
+    w, dw = oracle.q4_0_decode(case["w"], k)
+    rows = sample_rows(m, 8, seed=m)
+    ref = np.concatenate([oracle.gemm_rect(q, d, w, dw, r, r + 1, 0, n) for r in rows])
+    assert row_rel_err(yb[rows, 8:8 + n], ref) <= TIGHT
+
+
 @pytest.mark.parametrize("bits", [4, 8])
 def test_gemm_attn512_full_size(torch, bits):
     """The benchmarked workload, in the benchmarked launch configuration."""
