@@ -208,6 +208,11 @@ __global__ __launch_bounds__(512, 1) void wide_kernel(GemmProblem p, int tiles_m
     auto compute = [&](const uint8_t *wl, const uint8_t *A, const float *Da, int st) {
         if (4 * st + wk >= NG)
             return; // uniform per wave
+        // wave priority 1 for the stage's first two blocks, 0 for the last
+        // two: a wave that has reached the second half yields issue slots to
+        // one of its SIMD still in the first half, so the waves reach the
+        // stage barrier closer together (3-6% faster on attn512-like shapes)
+        __builtin_amdgcn_s_setprio(1);
         const uint8_t *W = wl + wk * C::kGroupBytes; // tile j at + j * kTileBytes
         // weight scales of the lane's column, four blocks per tile (fp16)
         uint2 hw[TN];
@@ -222,6 +227,8 @@ __global__ __launch_bounds__(512, 1) void wide_kernel(GemmProblem p, int tiles_m
         }
 #pragma unroll
         for (int q = 0; q < 4; q++) {
+            if (q == 2)
+                __builtin_amdgcn_s_setprio(0);
             const uint2 ad = *reinterpret_cast<const uint2 *>(A + a_rd[q]);
             Op a;
             a[0] = (int)act_lo(ad.x);
