@@ -111,10 +111,37 @@ def gemm_bytes(m, k, n, bits, experts=1, out_bytes=4):
     return experts * n * k * 18 // 32 + m * k * bits // 8 + m * (k // 32) * 4 + m * n * out_bytes
 
 
+def strip_comments(text):
+    """C++ source without its comments (string and character literals kept)
+    and with every run of whitespace made one space, so that an edit of
+    comments alone does not change the hash below."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        ch = text[i]
+        if ch in "\"'":
+            j = i + 1
+            while j < n and text[j] != ch:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+        else:
+            out.append(ch)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def source_hash():
+    """First 16 hex digits of sha256 over the GEMM kernel sources, comments
+    removed."""
     h = hashlib.sha256()
     for f in GEMM_SRCS:
-        h.update(open(f, "rb").read())
+        h.update(strip_comments(open(f, encoding="utf-8").read()).encode("utf-8"))
     return h.hexdigest()[:16]
 
 

@@ -1,5 +1,5 @@
-// strip.hip -- the dense W4A4 product on 32-row strips (gfx950, 4-bit
-// activations).
+// strip.hip -- the dense W4A4 product on 32-row strips (gfx950, 4- or
+// 8-bit activation codes).
 //
 // "509 tokens a second of prompt: the Hadamard route ships", section "Why
 // prompts are a matrix-unit problem": with hundreds of rows the product is
@@ -12,17 +12,20 @@
 //   - a workgroup owns 32 rows x 128 columns and has four waves; wave t owns
 //     32-column tile t over the whole of K, so no partial sums are added
 //     across waves and every output is one wave's in-order accumulation;
-//   - stages of 8 blocks, double-buffered (23 KB each), so that three
-//     workgroups share a CU and run independently: one computes while
-//     another waits at its barrier;
-//   - three waves per SIMD, so each block's epilogue follows its matrix
-//     instruction directly (other waves hide its latency); in the last
-//     stage, code chunks of blocks past K are written as zeros (a zero code
-//     makes the block product exactly zero whatever the weights), so the
-//     arithmetic always covers 8 blocks.
+//   - stages of 8 blocks with 4-bit codes, 4 with 8-bit codes (their rows
+//     take twice the bytes), double-buffered (23 / 14 KB per stage), so
+//     that three or more workgroups share a CU and run independently: one
+//     computes while another waits at its barrier;
+//   - three or more waves per SIMD, so each block's epilogue follows its
+//     matrix instruction directly (other waves hide its latency); in the
+//     last stage, code chunks of blocks past K are written as zeros (a zero
+//     code makes the block product exactly zero whatever the weights), so
+//     the arithmetic always covers whole stages.
 // Rows past M repeat the last row (never stored).  Where 64 x 160 tiles fit
 // and suit the shape, the wide kernel (wide.hip) is faster (fewer operand
-// reads per product); elsewhere this kernel beats 64 x 128 and smaller tiles.
+// reads per product); elsewhere this kernel beats 64 x 128 and smaller tiles,
+// and with 8-bit codes the tiled kernel (gemm.hip) wherever there are at
+// least three strips per CU.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 

@@ -1,0 +1,28 @@
+"""The kernel-source hash that keys the committed traffic counters ignores
+comments and whitespace and nothing else (host only)."""
+import os
+import sys
+
+sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+import bench  # noqa: E402
+
+
+def test_comments_and_whitespace_are_ignored():
+    a = "int f(int x) {\n    return x + 1; // add one\n}\n"
+    b = "/* f */ int f(int x)\n{\n  return x + 1;\n}\n"
+    assert bench.strip_comments(a) == bench.strip_comments(b)
+
+
+def test_code_and_literals_are_kept():
+    assert bench.strip_comments("return x + 1;") != bench.strip_comments("return x + 2;")
+    # comment markers inside literals are code
+    s = 'asm("v_mov // not a comment"); char c = \'/\';'
+    assert bench.strip_comments(s) == s
+    assert bench.strip_comments('a = "x"; // y') == 'a = "x";'
+
+
+def test_hash_is_stable_and_covers_the_kernels():
+    h = bench.source_hash()
+    assert len(h) == 16 and h == bench.source_hash()
+    names = {os.path.basename(f) for f in bench.GEMM_SRCS}
+    assert {"gemm.hip", "wide.hip", "strip.hip", "grouped.hip", "skinny.hip"} <= names
