@@ -179,7 +179,7 @@ def test_gemm_wide_tiles(torch, m, k, n, bits):
 
 @pytest.mark.parametrize("m,k,n", [(1000, 1056, 12288), (1000, 448, 12288), (2048, 160, 6144),
                                    (4096, 96, 17408), (1024, 32, 12288), (33, 32, 128),
-                                   (40, 1056, 256), (65, 640, 640)])
+                                   (40, 1056, 256), (65, 640, 640), (64, 32800, 256)])
 @pytest.mark.parametrize("bits", [4, 8])
 def test_gemm_strip_tiles(torch, m, k, n, bits):
     """4-bit shapes with more than 32 rows, N a multiple of 128 and 64 x 160
@@ -188,7 +188,8 @@ def test_gemm_strip_tiles(torch, m, k, n, bits):
     a last strip of one row: M = 33, 65), K with an odd number of 4-block
     groups and a one-block last stage (1056), an even number with a partial
     last group (448), one stage (160), one partial group (96) and a single
-    block (32); a few workgroups (M = 33, N = 128) up to thousands.  8-bit
+    block (32), and a long K (32800: 1025 blocks); a few workgroups (M = 33,
+    N = 128) up to thousands.  8-bit
     codes take stages of four blocks (one group) instead of eight."""
     case = synth.small_dense(m, k, n, seed=m + 5 * k + n)
     rows = sample_rows(m, 24, seed=m + k + 1)
