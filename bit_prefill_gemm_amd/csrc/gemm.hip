@@ -454,10 +454,18 @@ __global__ __launch_bounds__(C::kThreads, C::kOcc) void w4a4_kernel(GemmProblem 
         const float *Da = reinterpret_cast<const float *>(W + C::kLdsW);
         const float2 *Dw = reinterpret_cast<const float2 *>(W + C::kLdsW + C::kLdsDa);
         const int kvalid = B - kb0; // >= 1
+        // eight-wave workgroups: wave priority 1 for the first half of the
+        // wave's blocks of the stage, 0 for the second, so that the two waves
+        // of a SIMD reach the stage barrier closer together (2-3% on the
+        // 8-bit 64 x 160 shapes)
+        if (C::kWaves >= 8)
+            __builtin_amdgcn_s_setprio(1);
 
 #pragma unroll
         for (int kk = 0; kk < KC / WK; kk++) {
             const int kc = kk * WK + wk;
+            if (C::kWaves >= 8 && kk == (KC / WK) / 2)
+                __builtin_amdgcn_s_setprio(0);
             if (kc >= kvalid)
                 break;
             Op a[TM];
