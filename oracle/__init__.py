@@ -62,6 +62,9 @@ def _load():
         "orc_block_sums": (None, [_p, _p, _i64, _i64, _i64, _i64, _i64, _p]),
         "orc_gemm_rect": (None, [_p, _p, _p, _p, _i64, _i64, _i64, _i64, _i64, _p]),
         "orc_gemm_points": (None, [_p, _p, _p, _p, _i64, _p, _p, _i64, _p]),
+        "orc_gemm_abs_rect": (None, [_p, _p, _p, _p, _i64, _i64, _i64, _i64, _i64, _p]),
+        "orc_grouped_abs_points": (None, [_p, _p, _p, _i64, _p, _p, _i64, _i64, _p, _p, _i64,
+                                          _p]),
         "orc_grouped_points": (None, [_p, _p, _p, _i64, _p, _p, _i64, _i64, _p, _p, _i64, _p]),
         "orc_ref_points": (None, [_p, ctypes.c_int, _i64, _p, _p, _i64, _p, _p, _i64, _p]),
         "orc_num_threads": (ctypes.c_int, []),
@@ -201,6 +204,19 @@ def gemm_rect(q, da, w, dw, m0, m1, n0, n1) -> np.ndarray:
     return y
 
 
+def gemm_abs_rect(q, da, w, dw, m0, m1, n0, n1) -> np.ndarray:
+    """sum_b |da dw S| per output of the rectangle (the scale of the fp32 error bound)."""
+    q = np.ascontiguousarray(q, dtype=np.int8)
+    da = np.ascontiguousarray(da, dtype=np.float32)
+    w = np.ascontiguousarray(w, dtype=np.int8)
+    dw = np.ascontiguousarray(dw, dtype=np.float64)
+    k = q.shape[1]
+    assert w.shape[1] == k and 0 <= m0 <= m1 <= q.shape[0] and 0 <= n0 <= n1 <= w.shape[0]
+    a = np.empty((m1 - m0, n1 - n0), dtype=np.float64)
+    _load().orc_gemm_abs_rect(_ptr(q), _ptr(da), _ptr(w), _ptr(dw), k, m0, m1, n0, n1, _ptr(a))
+    return a
+
+
 def gemm_points(q, da, w, dw, rows, cols) -> np.ndarray:
     q = np.ascontiguousarray(q, dtype=np.int8)
     da = np.ascontiguousarray(da, dtype=np.float32)
@@ -232,6 +248,23 @@ def grouped_points(q, da, offsets, w, dw, rows, cols) -> np.ndarray:
     _load().orc_grouped_points(_ptr(q), _ptr(da), _ptr(off), E, _ptr(w), _ptr(dw), n, k,
                                _ptr(ri), _ptr(ci), ri.size, _ptr(y))
     return y
+
+
+def grouped_abs_points(q, da, offsets, w, dw, rows, cols) -> np.ndarray:
+    """As grouped_points, with sum_b |da dw S| in place of the output."""
+    q = np.ascontiguousarray(q, dtype=np.int8)
+    da = np.ascontiguousarray(da, dtype=np.float32)
+    off = np.ascontiguousarray(offsets, dtype=np.int32)
+    w = np.ascontiguousarray(w, dtype=np.int8)
+    dw = np.ascontiguousarray(dw, dtype=np.float64)
+    E, n, k = w.shape
+    assert off.shape == (E + 1,)
+    ri = np.ascontiguousarray(rows, dtype=np.int64)
+    ci = np.ascontiguousarray(cols, dtype=np.int64)
+    a = np.empty(ri.shape, dtype=np.float64)
+    _load().orc_grouped_abs_points(_ptr(q), _ptr(da), _ptr(off), E, _ptr(w), _ptr(dw), n, k,
+                                   _ptr(ri), _ptr(ci), ri.size, _ptr(a))
+    return a
 
 
 def ref_points(x, w, dw, rows, cols) -> np.ndarray:

@@ -489,6 +489,35 @@ void orc_gemm_rect(const int8_t *q, const float *da, const int8_t *w, const doub
             y[(r - m0) * nn + (c - n0)] = out_one(q, da, w, dw, k, r, c);
 }
 
+/*
+ * a[r][c] = sum_b |fp64(da[r][b]) * dw[c][b] * S[r][c][b]|: the sum of the
+ * magnitudes of the terms whose sum is y[r][c].  Every fp32 evaluation of
+ * that sum (two-sided block scaling of exact block sums, accumulated in any
+ * order) is within a small multiple of 2^-24 * a of the exact y, so a is the
+ * scale of an element-wise error bound.
+ */
+static double out_abs_one(const int8_t *q, const float *da, const int8_t *w, const double *dw,
+                          int64_t k, int64_t r, int64_t c)
+{
+    const int64_t nb = k / QK;
+    double a = 0.0;
+    for (int64_t b = 0; b < nb; b++) {
+        int32_t s = block_dot(q + r * k + b * QK, w + c * k + b * QK);
+        a += fabs((double)da[r * nb + b] * dw[c * nb + b] * (double)s);
+    }
+    return a;
+}
+
+void orc_gemm_abs_rect(const int8_t *q, const float *da, const int8_t *w, const double *dw,
+                       int64_t k, int64_t m0, int64_t m1, int64_t n0, int64_t n1, double *a)
+{
+    const int64_t nn = n1 - n0;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = m0; r < m1; r++)
+        for (int64_t c = n0; c < n1; c++)
+            a[(r - m0) * nn + (c - n0)] = out_abs_one(q, da, w, dw, k, r, c);
+}
+
 void orc_gemm_points(const int8_t *q, const float *da, const int8_t *w, const double *dw,
                      int64_t k, const int64_t *ri, const int64_t *ci, int64_t npts, double *y)
 {
@@ -520,6 +549,24 @@ void orc_grouped_points(const int8_t *q, const float *da, const int32_t *off, in
             continue;
         }
         y[p] = out_one(q, da, w + e * n * k, dw + e * n * nb, k, r, ci[p]);
+    }
+}
+
+/* As orc_grouped_points, with the magnitude sum of out_abs_one (NAN outside). */
+void orc_grouped_abs_points(const int8_t *q, const float *da, const int32_t *off, int64_t E,
+                            const int8_t *w, const double *dw, int64_t n, int64_t k,
+                            const int64_t *ri, const int64_t *ci, int64_t npts, double *a)
+{
+    const int64_t nb = k / QK;
+#pragma omp parallel for schedule(static)
+    for (int64_t p = 0; p < npts; p++) {
+        int64_t r = ri[p], e = -1;
+        for (int64_t t = 0; t < E; t++)
+            if (r >= off[t] && r < off[t + 1]) {
+                e = t;
+                break;
+            }
+        a[p] = e < 0 ? NAN : out_abs_one(q, da, w + e * n * k, dw + e * n * nb, k, r, ci[p]);
     }
 }
 

@@ -305,6 +305,32 @@ def test_gemm_matches_numpy_formula():
     assert np.array_equal(pts, y[[0, 11, 5], [39, 0, 17]])
 
 
+def test_abs_sum_matches_numpy_and_bounds_output():
+    """sum_b |da dw S|: numpy from integer block products; it bounds |y|, and
+    it equals y where every term is non-negative (all codes and scales >= 0)."""
+    case, q, da, w, dw = _small_case(8, 192, 24, 19)
+    a = oracle.gemm_abs_rect(q, da, w, dw, 0, 8, 0, 24)
+    S = np.stack([q.reshape(8, 6, 32)[:, b].astype(np.int64)
+                  @ w.reshape(24, 6, 32)[:, b].astype(np.int64).T for b in range(6)], axis=2)
+    ref = np.abs(da.astype(np.float64)[:, None, :] * dw[None, :, :] * S).sum(axis=2)
+    assert np.allclose(a, ref, rtol=1e-14, atol=0)
+    y = oracle.gemm_rect(q, da, w, dw, 0, 8, 0, 24)
+    assert np.all(np.abs(y) <= a * (1 + 1e-14))
+    assert np.array_equal(oracle.gemm_abs_rect(q, da, w, dw, 2, 5, 3, 20), a[2:5, 3:20])
+    qp, wp = np.abs(q), np.abs(w)
+    assert np.array_equal(oracle.gemm_abs_rect(qp, da, wp, dw, 0, 8, 0, 24),
+                          oracle.gemm_rect(qp, da, wp, dw, 0, 8, 0, 24))
+    # the grouped form selects the row's expert like grouped_points
+    off = np.array([0, 5, 8], dtype=np.int32)
+    wg = np.stack([w[:12], w[12:]])
+    dwg = np.stack([dw[:12], dw[12:]])
+    rows, cols = np.repeat(np.arange(9), 12), np.tile(np.arange(12), 9)
+    ag = oracle.grouped_abs_points(q, da, off, wg, dwg, rows[:96], cols[:96]).reshape(8, 12)
+    assert np.allclose(ag[:5], a[:5, :12], rtol=1e-14, atol=0)
+    assert np.allclose(ag[5:], a[5:, 12:], rtol=1e-14, atol=0)
+    assert np.isnan(oracle.grouped_abs_points(q, da, off, wg, dwg, [8], [0])[0])
+
+
 def test_bruteforce_2x32x2():
     """Literal loops from the dense matrix: one block, so y = da dw S exactly."""
     rng = np.random.default_rng(13)
