@@ -20,14 +20,19 @@ weighted combine; `kernel_us` gives each kernel's own duration).
 Prints ONE JSON line.  `value` is prompt tokens per second of the step.  The
 `roofline` object covers the GEMM kernel (the dominant kernel).  Its average
 duration is measured with HIP events recorded on the launch stream around
-every 8th GEMM of the timed region.  The bound is whichever algorithmic floor is
-larger: the fp32 VALU epilogue (two FMAs per output element and 32-block)
-against the fp32 vector peak (dense shapes with many rows), or the HBM bytes
-against the HBM peak (a few rows, and the grouped expert GEMMs, whose weight
-stream is larger); the int8 matrix-core view (effective TOPS against the
-dense int8 peak) is reported beside it.
+every 8th GEMM of the timed region.  The bound is whichever algorithmic floor
+of the contraction is larger: its 2*M*N*K integer ops at the dense int8
+matrix peak ("mfma"), or its HBM bytes at the HBM peak ("hbm": a few rows, and
+the grouped expert GEMMs, whose weight stream is larger).  `epilogue_valu`
+gives the same launch against the other floor this method has on gfx950: the
+fp32 epilogue (two FMAs per output element and 32-block) at the fp32 vector
+peak.
 `traffic` comes from the committed rocprofv3 counter summary for this kernel
-and workload, and is null if the kernel source changed since it was taken.
+and workload, and is null if the kernel source or its compile flags changed
+since it was taken.
+`configs` (default workload only) measures every other workload in the same
+run, with fewer steps and no CPU baseline: GEMM time, kernel, roofline
+fraction and tokens/s of each.
 `cpu_baseline` times the CPU oracle on the same workload (test
 infrastructure, not the product path).
 
@@ -79,10 +84,15 @@ WORKLOADS = {
     "moe512_layer": dict(m=512, k=2048, n=2048, experts=128, tokens=512, layer=True),
 }
 # kernel sources of the GEMM paths (the tiled, wide, strip and grouped kernels,
-# and the weight-stream kernel used for a few rows)
+# the weight-stream kernel used for a few rows, and the headers they share)
 GEMM_SRCS = [os.path.join(ROOT, "bit_prefill_gemm_amd", "csrc", f)
              for f in ("gemm.hip", "skinny.hip", "wide.hip", "strip.hip", "grouped.hip",
-                       "operands.h")]
+                       "operands.h", "internal.h")]
+# the workloads measured beside the default one (name, activation bits)
+CONFIG_RUNS = [("attn512", 8), ("ffn512_gate", 4), ("ffn512_down", 4), ("ffn512_gate", 8),
+               ("ffn512_down", 8), ("long1024", 4), ("long1024", 8), ("moe512_gu", 4),
+               ("moe512_dn", 4), ("moe512_layer", 4), ("m16_gate", 4), ("m16_down", 4),
+               ("m16_attn", 4)]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_traffic.json")
 # timed steps between two whose GEMM is bracketed by events
 EVENT_EVERY = 8
@@ -100,6 +110,9 @@ def parse():
     ap.add_argument("--cold-bytes", type=float, default=512e6,
                     help="total bytes of distinct input copies cycled through")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the other workloads (measured only with the default one)")
+    ap.add_argument("--config-steps", type=int, default=40)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration", type=float, default=0.0)
     return ap.parse_args()
@@ -137,12 +150,24 @@ def strip_comments(text):
 
 
 def source_hash():
-    """First 16 hex digits of sha256 over the GEMM kernel sources, comments
-    removed."""
+    """First 16 hex digits of sha256 over the GEMM kernel sources (comments
+    removed) and the flags they are compiled with."""
+    from bit_prefill_gemm_amd.build import KERNEL_FLAGS
     h = hashlib.sha256()
     for f in GEMM_SRCS:
         h.update(strip_comments(open(f, encoding="utf-8").read()).encode("utf-8"))
+    h.update(" ".join(KERNEL_FLAGS).encode("utf-8"))
     return h.hexdigest()[:16]
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def measured_traffic(workload, bits, out="f32"):
@@ -182,24 +207,32 @@ def cpu_baseline(data, wl, name, bits, seconds):
         if el >= seconds or reps >= 50:
             break
     return {"value": reps * m / el, "unit": "tokens/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
+            "cpu": cpu_model(), "kind": "oracle",
             "sample": "whole %s workload (quantize %dx%d, then %dx%dx%d GEMM with fp64 "
                       "output), %d repetition(s) in %.1f s" % (name, m, k, m, k, n, reps, el)}
 
 
 def roofline_of(kernel, m, k, n, bits, experts, seconds, traffic, out_bytes=4):
-    """The binding roofline of one GEMM launch: whichever algorithmic floor is
-    larger, the HBM bytes at 8 TB/s or the fp32 epilogue (two FMAs per output
-    and block) at the fp32 vector peak."""
+    """The binding roofline of one GEMM launch: whichever algorithmic floor of
+    the contraction is larger, its 2*M*N*K int8 matrix ops at the dense int8
+    peak or its HBM bytes at 8 TB/s."""
     gbytes = gemm_bytes(m, k, n, bits, experts, out_bytes)
-    epi_flops = 4.0 * m * n * (k // 32)
-    if gbytes / PEAK_HBM >= epi_flops / PEAK_FP32_FLOPS:
+    ops = 2.0 * m * n * k
+    if gbytes / PEAK_HBM >= ops / PEAK_INT8_OPS:
         return {"bound": "hbm", "achieved": gbytes / seconds / 1e9, "peak": PEAK_HBM / 1e9,
                 "unit": "GB/s", "frac": gbytes / seconds / PEAK_HBM, "traffic": traffic,
                 "kernel": kernel}
-    return {"bound": "alu", "achieved": epi_flops / seconds / 1e12,
-            "peak": PEAK_FP32_FLOPS / 1e12, "unit": "TFLOP/s",
-            "frac": epi_flops / seconds / PEAK_FP32_FLOPS, "traffic": traffic, "kernel": kernel}
+    return {"bound": "mfma", "achieved": ops / seconds / 1e12, "peak": PEAK_INT8_OPS / 1e12,
+            "unit": "TOP/s", "frac": ops / seconds / PEAK_INT8_OPS, "traffic": traffic,
+            "kernel": kernel}
+
+
+def epilogue_of(m, k, n, seconds):
+    """The same launch against the fp32 epilogue floor: two FMAs (4 flops) per
+    output element and 32-block at the fp32 vector peak."""
+    flops = 4.0 * m * n * (k // 32)
+    return {"achieved": flops / seconds / 1e12, "peak": PEAK_FP32_FLOPS / 1e12,
+            "unit": "TFLOP/s", "frac": flops / seconds / PEAK_FP32_FLOPS}
 
 
 def copy_calibration(nbytes):
@@ -212,31 +245,24 @@ def copy_calibration(nbytes):
     torch.cuda.synchronize()
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(run with --gpus 1)", file=sys.stderr)
-        sys.exit(2)
+def load_data(name, cache):
+    from bit_prefill_gemm_amd import synth
+    if name not in cache:
+        cache[name] = synth.make(name)
+    return cache[name]
 
+
+def run_gemm(workload, bits, out_kind, steps, warmup, cold_bytes, cache, event_every=EVENT_EVERY):
+    """quantize_act_h32 + w4a4_gemm (or the grouped product) on one workload:
+    `steps` timed steps after `warmup`, cycling cold copies of the inputs."""
     import torch
 
     from bit_prefill_gemm_amd import binding as bb
-    from bit_prefill_gemm_amd import synth
 
-    if not torch.cuda.is_available():
-        print("no GPU visible", file=sys.stderr)
-        sys.exit(1)
-    if args.copy_calibration:
-        copy_calibration(args.copy_calibration)
-        return
-    bb.lib()
-    wl = WORKLOADS[args.workload]
-    if wl.get("layer"):
-        return main_layer(args, wl)
-    m, k, n, bits = wl["m"], wl["k"], wl["n"], args.bits
+    wl = WORKLOADS[workload]
+    m, k, n = wl["m"], wl["k"], wl["n"]
     experts = wl.get("experts", 1)
-    data = synth.make(wl.get("src", args.workload))
+    data = load_data(wl.get("src", workload), cache)
     W0 = bb.rotate_pack_weights(data[wl.get("w", "w")], bb.SRC_Q4_0_ROTATED, n, k, experts)
 
     dev = torch.device("cuda:0")
@@ -245,16 +271,20 @@ def main():
                if experts > 1 else None)
     img0 = torch.from_numpy(W0.image).to(dev)
     per_copy = img0.numel() + x0.numel() * 2
-    copies = max(1, int(math.ceil(args.cold_bytes / per_copy)))
+    copies = max(1, int(math.ceil(cold_bytes / per_copy)))
     imgs = [img0] + [img0.clone() for _ in range(copies - 1)]
     xs = [x0] + [x0.clone() for _ in range(copies - 1)]
     Ws = [bb.Weights(W0.desc, im) for im in imgs]
     codes = torch.empty((m, k // 2 if bits == 4 else k), dtype=torch.uint8, device=dev)
     scales = torch.empty((m, k // 32), dtype=torch.float32, device=dev)
-    bf16_out = args.out == "bf16"
+    bf16_out = out_kind == "bf16"
     out_bytes = 2 if bf16_out else 4
     y = torch.empty((m, n), dtype=torch.bfloat16 if bf16_out else torch.float32, device=dev)
     stream = torch.cuda.Stream(device=dev)
+    if offsets is None:
+        kname = bb.w4a4_gemm_kernel_name(bits, m, W0)
+    else:
+        kname = bb.w4a4_grouped_gemm_kernel_name(bits, m, W0)
 
     def quantize(j):
         bb.quantize_act_h32(xs[j], bits, codes=codes, scales=scales, stream=stream)
@@ -268,71 +298,58 @@ def main():
             f(codes, scales, bits, offsets, Ws[j], y=y, stream=stream)
 
     # The GEMM's duration is taken with two events around it on every
-    # EVENT_EVERY-th timed step: each recorded event is one more packet on the
+    # event_every-th timed step: each recorded event is one more packet on the
     # queue and costs the step several microseconds, so recording them on
     # every step would inflate the step time.  The quantizer's own duration
     # is taken after the timed region, with events around it alone.
     with torch.cuda.stream(stream):
-        for i in range(args.warmup):
+        for i in range(warmup):
             quantize(i % copies)
             gemm(i % copies)
         torch.cuda.synchronize()
         evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(2))
-               for _ in range(0, args.steps, EVENT_EVERY)]
+               for _ in range(0, steps, event_every)]
         t0 = time.perf_counter()
-        for i in range(args.steps):
-            j = (args.warmup + i) % copies
+        for i in range(steps):
+            j = (warmup + i) % copies
             quantize(j)
-            if i % EVENT_EVERY == 0:
-                evs[i // EVENT_EVERY][0].record(stream)
+            if i % event_every == 0:
+                evs[i // event_every][0].record(stream)
                 gemm(j)
-                evs[i // EVENT_EVERY][1].record(stream)
+                evs[i // event_every][1].record(stream)
             else:
                 gemm(j)
         torch.cuda.synchronize()
         t1 = time.perf_counter()
         qevs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(2))
-                for _ in range(min(args.steps, 50))]
+                for _ in range(min(steps, 50))]
         for i, (e0, e1) in enumerate(qevs):
             e0.record(stream)
             quantize(i % copies)
             e1.record(stream)
         torch.cuda.synchronize()
 
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    ms_per_step = (t1 - t0) * 1e3 / steps
     quant_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in qevs]))
     gemm_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
     gemm_s = gemm_ms * 1e-3
-    ops = 2.0 * m * n * k
-    eff_tops = ops / gemm_s / 1e12
+    eff_tops = 2.0 * m * n * k / gemm_s / 1e12
     gbytes = gemm_bytes(m, k, n, bits, experts, out_bytes)
-    traffic = measured_traffic(args.workload, bits, args.out)
-
-    kernel = ("w4a4_gemm" if experts == 1 else "w4a4_grouped_gemm") + ("_bf16" if bf16_out else "")
-    roofline = roofline_of(kernel, m, k, n, bits, experts, gemm_s, traffic, out_bytes)
-
-    out = {
-        "metric": "prompt tokens/s + effective TOPS (% int8 MFMA peak) for rotated W4A4 GEMM, M=512",
+    traffic = measured_traffic(workload, bits, out_kind)
+    entry = ("w4a4_gemm" if experts == 1 else "w4a4_grouped_gemm") + ("_bf16" if bf16_out else "")
+    res = {
         "value": wl.get("tokens", m) / (ms_per_step * 1e-3),
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
         "ms_per_step": ms_per_step,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "i8" if bits == 8 else "i4",
-        "data": "synthetic",
         "config": {"workload": "%s: M=%d K=%d N=%d%s, bf16 activations, rotated Q4_0 weights, "
                                "%d-bit activation codes"
-                               % (args.workload, m, k, n,
+                               % (workload, m, k, n,
                                   ", %d experts (grouped)" % experts if experts > 1 else "", bits),
                    "m": m, "k": k, "n": n, "experts": experts, "act_bits": bits,
-                   "out": args.out, "cold_copies": copies},
-        "roofline": roofline,
-        "int8_mfma": {"achieved": eff_tops, "peak": PEAK_INT8_OPS / 1e12, "unit": "TOP/s",
-                      "frac": eff_tops / (PEAK_INT8_OPS / 1e12)},
+                   "out": out_kind, "cold_copies": copies},
+        "roofline": roofline_of(entry + ": " + kname, m, k, n, bits, experts, gemm_s, traffic,
+                                out_bytes),
+        "epilogue_valu": epilogue_of(m, k, n, gemm_s),
+        "kernel": kname,
         "eff_TOPS": eff_tops,
         "pct_int8_peak": 100.0 * eff_tops / (PEAK_INT8_OPS / 1e12),
         "gemm_us": gemm_ms * 1e3,
@@ -341,14 +358,93 @@ def main():
         "gemm_hbm_GBps": gbytes / gemm_s / 1e9,
         "pct_hbm": 100.0 * gbytes / gemm_s / PEAK_HBM,
         "gemm_algorithmic_bytes": gbytes,
-        "gemm_source_sha256_16": source_hash(),
     }
+    del imgs, xs, Ws, img0, x0, codes, scales, y
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res, data
+
+
+def summary(res):
+    """The per-workload entry of `configs`."""
+    if "kernel_us" in res:
+        return {"step_us": res["step_us"], "tokens_per_s": res["value"],
+                "kernel_us": res["kernel_us"], "roofline": res["roofline"]}
+    r = res["roofline"]
+    return {"kernel": res["kernel"], "gemm_us": res["gemm_us"], "quant_us": res["quant_us"],
+            "step_us": res["step_us"], "tokens_per_s": res["value"],
+            "roofline": {"bound": r["bound"], "frac": r["frac"], "achieved": r["achieved"],
+                         "unit": r["unit"], "traffic": r["traffic"]},
+            "int8_frac": res["pct_int8_peak"] / 100.0, "hbm_frac": res["pct_hbm"] / 100.0,
+            "epilogue_valu_frac": res["epilogue_valu"]["frac"]}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from bit_prefill_gemm_amd import binding as bb
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
+    bb.lib()
+    wl = WORKLOADS[args.workload]
+    cache = {}
+    if wl.get("layer"):
+        res, data = run_layer(args.bits, args.steps, args.warmup, args.cold_bytes, cache)
+    else:
+        res, data = run_gemm(args.workload, args.bits, args.out, args.steps, args.warmup,
+                             args.cold_bytes, cache)
+    out = {
+        "metric": "prompt tokens/s + effective TOPS (% int8 MFMA peak) for rotated W4A4 GEMM, M=512",
+        "value": res["value"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": res["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i8" if args.bits == 8 else "i4",
+        "data": "synthetic",
+    }
+    out.update({kk: v for kk, v in res.items() if kk not in ("value", "ms_per_step")})
+    out["gemm_source_sha256_16"] = source_hash()
+    if args.workload == "attn512" and not args.no_configs:
+        configs = {}
+        for name, bits in CONFIG_RUNS:
+            if (name, bits) == (args.workload, args.bits):
+                continue
+            print("config %s %d-bit" % (name, bits), file=sys.stderr, flush=True)
+            if WORKLOADS[name].get("layer"):
+                r, _ = run_layer(bits, args.config_steps, 5, args.cold_bytes, cache)
+            else:
+                r, _ = run_gemm(name, bits, "f32", args.config_steps, 5, args.cold_bytes, cache,
+                                event_every=4)
+            configs["%s/%d" % (name, bits)] = summary(r)
+        out["configs"] = configs
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(data, wl, args.workload, bits, args.cpu_seconds)
+        if wl.get("layer"):
+            out["cpu_baseline"] = cpu_baseline_layer(data, res["routes"][0], res["routes"][1],
+                                                     args.bits, args.cpu_seconds)
+        else:
+            out["cpu_baseline"] = cpu_baseline(data, wl, args.workload, args.bits,
+                                               args.cpu_seconds)
+    out.pop("routes", None)
     print(json.dumps(out))
 
 
-def main_layer(args, wl):
+def run_layer(bits, steps, warmup, cold_bytes, cache):
     """One step = one expert layer over 512 tokens (moe512: hidden 2048, 128
     experts, top-8, expert intermediate 768)."""
     import torch
@@ -356,8 +452,7 @@ def main_layer(args, wl):
     from bit_prefill_gemm_amd import binding as bb
     from bit_prefill_gemm_amd import synth
 
-    bits = args.bits
-    data = synth.make("moe512")
+    data = load_data("moe512", cache)
     c = data["cfg"]
     T, H, E, K8, I = c["tokens"], c["hidden"], c["experts"], c["topk"], c["inter"]
     rows = T * K8
@@ -369,7 +464,7 @@ def main_layer(args, wl):
     dn_img = torch.from_numpy(Wdn0.image).to(dev)
     x0 = torch.from_numpy(data["x_tokens"].view(np.int16)).to(dev).view(torch.bfloat16)
     per_copy = gu_img.numel() + dn_img.numel() + x0.numel() * 2
-    copies = max(1, int(math.ceil(args.cold_bytes / per_copy)))
+    copies = max(1, int(math.ceil(cold_bytes / per_copy)))
     Wgu = [bb.Weights(Wgu0.desc, gu_img if j == 0 else gu_img.clone()) for j in range(copies)]
     Wdn = [bb.Weights(Wdn0.desc, dn_img if j == 0 else dn_img.clone()) for j in range(copies)]
     xs = [x0 if j == 0 else x0.clone() for j in range(copies)]
@@ -421,19 +516,19 @@ def main_layer(args, wl):
                 f(j)
 
     with torch.cuda.stream(stream):
-        for i in range(args.warmup):
+        for i in range(warmup):
             step(i % copies)
         torch.cuda.synchronize()
         gate_evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(2))
-                    for _ in range(0, args.steps, EVENT_EVERY)]
+                    for _ in range(0, steps, EVENT_EVERY)]
         t0 = time.perf_counter()
-        for i in range(args.steps):
-            step((args.warmup + i) % copies,
+        for i in range(steps):
+            step((warmup + i) % copies,
                  gate_evs[i // EVENT_EVERY] if i % EVENT_EVERY == 0 else None)
         torch.cuda.synchronize()
         t1 = time.perf_counter()
         # each kernel's own duration: event pairs around it alone, in step order
-        reps = min(args.steps, 30)
+        reps = min(steps, 30)
         evs = {name: [] for name in kernels}
         for i in range(reps):
             j = i % copies
@@ -446,22 +541,14 @@ def main_layer(args, wl):
         torch.cuda.synchronize()
     kernel_us = {name: 1e3 * float(np.mean([a.elapsed_time(b) for a, b in v]))
                  for name, v in evs.items()}
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    ms_per_step = (t1 - t0) * 1e3 / steps
     gate_s = float(np.mean([a.elapsed_time(b) for a, b in gate_evs])) * 1e-3
-    roofline = roofline_of("w4a4_grouped_gemm_gather", rows, H, 2 * I, bits, E, gate_s, None)
-    out = {
-        "metric": "prompt tokens/s + effective TOPS (% int8 MFMA peak) for rotated W4A4 GEMM, M=512",
+    kname = bb.w4a4_grouped_gemm_kernel_name(bits, rows, Wgu0, src_rows=T)
+    roofline = roofline_of("w4a4_grouped_gemm_gather: " + kname, rows, H, 2 * I, bits, E, gate_s,
+                           None)
+    res = {
         "value": T / (ms_per_step * 1e-3),
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
         "ms_per_step": ms_per_step,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "i8" if bits == 8 else "i4",
-        "data": "synthetic",
         "config": {"workload": "moe512_layer: expert layer over %d tokens, hidden %d, %d experts, "
                                "top-%d, expert intermediate %d, bf16 activations, rotated Q4_0 "
                                "weights, %d-bit activation codes" % (T, H, E, K8, I, bits),
@@ -470,11 +557,12 @@ def main_layer(args, wl):
         "roofline": roofline,
         "kernel_us": kernel_us,
         "step_us": ms_per_step * 1e3,
-        "gemm_source_sha256_16": source_hash(),
+        "routes": (e_np, w_np),
     }
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline_layer(data, e_np, w_np, bits, args.cpu_seconds)
-    print(json.dumps(out))
+    del Wgu, Wdn, xs, gu_img, dn_img, x0
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res, data
 
 
 def cpu_baseline_layer(data, e_np, w_np, bits, seconds):
@@ -510,7 +598,7 @@ def cpu_baseline_layer(data, e_np, w_np, bits, seconds):
         if el >= seconds or reps >= 20:
             break
     return {"value": reps * T / el, "unit": "tokens/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
+            "cpu": cpu_model(), "kind": "oracle",
             "sample": "whole moe512 expert layer (sort, quantize, gate/up, SwiGLU-quantize, "
                       "down, combine), %d repetition(s) in %.1f s" % (reps, el)}
 

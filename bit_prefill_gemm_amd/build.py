@@ -17,14 +17,16 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libbpg.so")
 SOURCES = ["api.hip", "quantize.hip", "gemm.hip", "skinny.hip", "wide.hip", "strip.hip", "grouped.hip", "moe.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-FLAGS = [
+# code-generation flags (the part of the command line that shapes the kernels;
+# the include directories below are paths of this checkout)
+KERNEL_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     # matrix-instruction results in ordinary VGPRs: the epilogues read them with
     # VALU instructions, which cannot read accumulation registers
     "-mllvm", "-amdgpu-mfma-vgpr-form",
-    "-Wall", "-Wno-unused-function", "-I", INCLUDE, "-I", CSRC,
 ]
+FLAGS = KERNEL_FLAGS + ["-Wall", "-Wno-unused-function", "-I", INCLUDE, "-I", CSRC]
 
 
 def _run(cmd):

@@ -421,6 +421,41 @@ bpg_status quantize_act_rot(const void *x, bpg_x_dtype dt, int64_t m, int64_t k,
     return quantize_checked(x, dt, m, k, ldx, act_bits, codes, scales, stream, rotation);
 }
 
+const char *w4a4_gemm_kernel_name(int act_bits, int64_t m, const bpg_weights_desc *w)
+{
+    if (!w || (act_bits != 4 && act_bits != 8) || m < 0 || m > ((int64_t)1 << 31) - 1)
+        return nullptr;
+    if (check_stamp(w, w->rotation) != BPG_OK || w->num_experts != 1)
+        return nullptr;
+    bpg::GemmProblem p{};
+    p.rows = m;
+    p.n = w->n;
+    p.k = w->k;
+    p.experts = 1;
+    p.act_bits = act_bits;
+    return bpg::kernel_name(bpg::plan_gemm(p));
+}
+
+const char *w4a4_grouped_gemm_kernel_name(int act_bits, int64_t total_rows, int64_t src_rows,
+                                          const bpg_weights_desc *w)
+{
+    if (!w || (act_bits != 4 && act_bits != 8) || total_rows < 0 ||
+        total_rows > ((int64_t)1 << 31) - 1 || src_rows < 0)
+        return nullptr;
+    if (check_stamp(w) != BPG_OK)
+        return nullptr;
+    static const int32_t kNotRead = 0; // stands for a row index: only tested for presence
+    bpg::GemmProblem p{};
+    p.rows = total_rows;
+    p.n = w->n;
+    p.k = w->k;
+    p.experts = w->num_experts;
+    p.act_bits = act_bits;
+    p.row_ids = src_rows > 0 ? &kNotRead : nullptr;
+    p.src_rows = src_rows;
+    return bpg::kernel_name(bpg::plan_grouped_gemm(p));
+}
+
 bpg_status w4a4_gemm_rot(const void *codes, const float *scales, int act_bits, int rotation,
                          int64_t m, const bpg_weights_desc *w, const void *w_dev, float *y,
                          int64_t ldy, void *stream)

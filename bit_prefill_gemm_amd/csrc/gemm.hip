@@ -678,16 +678,17 @@ double est_cfg(int64_t m, int64_t n)
     return rounds * cost * (C::kWaves * C::kOcc / 4.0);
 }
 
+// The kernel a dense problem runs (decided on the host from the shape alone,
+// so the routing query below names exactly what launch_gemm launches).
 template <int BITS>
-hipError_t launch_dense_bits(const GemmProblem &p, hipStream_t stream)
+int plan_dense_bits(const GemmProblem &p)
 {
     using T = Tiles<BITS>;
     const int64_t m = p.rows, n = p.n;
-    if (m <= 16) {
-        if (est_cfg<typename T::T16x64>(m, n) <= est_cfg<typename T::T16x32>(m, n))
-            return launch_dense_cfg<typename T::T16x64>(p, stream);
-        return launch_dense_cfg<typename T::T16x32>(p, stream);
-    }
+    if (m <= 16)
+        return est_cfg<typename T::T16x64>(m, n) <= est_cfg<typename T::T16x32>(m, n)
+                   ? kTiled16x64
+                   : kTiled16x32;
     const double e[4] = {est_cfg<typename T::W64x160>(m, n), est_cfg<typename T::W64x128>(m, n),
                          est_cfg<typename T::T64x64>(m, n), est_cfg<typename T::T64x32>(m, n)};
     int best = 3;
@@ -704,15 +705,27 @@ hipError_t launch_dense_bits(const GemmProblem &p, hipStream_t stream)
     // strips than three per CU: there the tiled kernel's K-split workgroups
     // fill every CU and the strips do not (M = 512, K = 17408, N = 5120).
     if (BITS == 4 && best == 0 && wide_fits(p))
-        return launch_wide(p, stream);
+        return kWide;
     if (strip_fits(p) &&
         (BITS == 4 || best != 0 || (p.rows + 31) / 32 * (p.n / 128) >= 3 * kCUs))
-        return launch_strip(p, stream);
-    switch (best) {
-    case 0: return launch_dense_cfg<typename T::W64x160>(p, stream);
-    case 1: return launch_dense_cfg<typename T::W64x128>(p, stream);
-    case 2: return launch_dense_cfg<typename T::T64x64>(p, stream);
-    default: return launch_dense_cfg<typename T::T64x32>(p, stream);
+        return kStrip;
+    static const int tiled[4] = {kTiled64x160, kTiled64x128, kTiled64x64, kTiled64x32};
+    return tiled[best];
+}
+
+template <int BITS>
+hipError_t launch_dense_bits(int kernel, const GemmProblem &p, hipStream_t stream)
+{
+    using T = Tiles<BITS>;
+    switch (kernel) {
+    case kWide: return launch_wide(p, stream);
+    case kStrip: return launch_strip(p, stream);
+    case kTiled64x160: return launch_dense_cfg<typename T::W64x160>(p, stream);
+    case kTiled64x128: return launch_dense_cfg<typename T::W64x128>(p, stream);
+    case kTiled64x64: return launch_dense_cfg<typename T::T64x64>(p, stream);
+    case kTiled64x32: return launch_dense_cfg<typename T::T64x32>(p, stream);
+    case kTiled16x64: return launch_dense_cfg<typename T::T16x64>(p, stream);
+    default: return launch_dense_cfg<typename T::T16x32>(p, stream);
     }
 }
 
@@ -720,26 +733,36 @@ hipError_t launch_dense_bits(const GemmProblem &p, hipStream_t stream)
 // 128 columns per workgroup: four waves of 32 x 32, each over the whole of K
 // (an expert's K is short, so splitting it across waves would leave each wave
 // too few blocks to amortise its set-up and the final reduction).
-template <int BITS>
-hipError_t launch_grouped_bits(const GemmProblem &p, hipStream_t stream)
-{
+// Grouped: 32-row slots (row tiles past an expert's rows are skipped) and
+// 128, 64 or 32 columns per workgroup: four waves of 32 x 32, each over the
+// whole of K (an expert's K is short, so splitting it across waves would leave
+// each wave too few blocks to amortise its set-up and the final reduction).
+template <int BITS> struct GroupedTiles {
     using C128 = Cfg<BITS, 16, 2, 2, 1, 4, 1, 4>; // 32 x 128
     using C64 = Cfg<BITS, 16, 2, 2, 1, 2, 1, 4>;  // 32 x 64
     using C32 = Cfg<BITS, 16, 2, 2, 1, 1, 1, 4>;  // 32 x 32
+};
+
+template <class C>
+hipError_t launch_grouped_cfg(const GemmProblem &p, hipStream_t stream)
+{
     // every expert needs ceil(rows_e / BM) slots: bounded by both of these
-    int64_t slots = (p.rows + p.experts * (C128::BM - 1)) / C128::BM;
+    int64_t slots = (p.rows + p.experts * (C::BM - 1)) / C::BM;
     if (slots > p.rows)
         slots = p.rows;
-    if (p.n % C128::BN == 0) {
-        const int tn = (int)(p.n / C128::BN);
-        return launch_cfg<C128, kGrouped>(p, 0, tn, 0, 0, slots * tn, stream);
+    const int tn = (int)(p.n / C::BN);
+    return launch_cfg<C, kGrouped>(p, 0, tn, 0, 0, slots * tn, stream);
+}
+
+template <int BITS>
+hipError_t launch_grouped_bits(int kernel, const GemmProblem &p, hipStream_t stream)
+{
+    using T = GroupedTiles<BITS>;
+    switch (kernel) {
+    case kGrouped128: return launch_grouped_cfg<typename T::C128>(p, stream);
+    case kGrouped64: return launch_grouped_cfg<typename T::C64>(p, stream);
+    default: return launch_grouped_cfg<typename T::C32>(p, stream);
     }
-    if (p.n % C64::BN == 0) {
-        const int tn = (int)(p.n / C64::BN);
-        return launch_cfg<C64, kGrouped>(p, 0, tn, 0, 0, slots * tn, stream);
-    }
-    const int tn = (int)(p.n / C32::BN);
-    return launch_cfg<C32, kGrouped>(p, 0, tn, 0, 0, slots * tn, stream);
 }
 
 template <int BITS>
@@ -755,22 +778,64 @@ hipError_t launch_sums_bits(const GemmProblem &p, hipStream_t stream)
 
 } // namespace
 
-hipError_t launch_gemm(const GemmProblem &p, hipStream_t stream)
+int plan_gemm(const GemmProblem &p)
 {
     if (p.rows == 0)
-        return hipSuccess;
+        return kNoKernel;
     if (skinny_fits(p))
+        return kSkinny;
+    return p.act_bits == 4 ? plan_dense_bits<4>(p) : plan_dense_bits<8>(p);
+}
+
+int plan_grouped_gemm(const GemmProblem &p)
+{
+    if (p.rows == 0)
+        return kNoKernel;
+    if (grouped_wide_fits(p))
+        return kSlot;
+    return p.n % 128 == 0 ? kGrouped128 : p.n % 64 == 0 ? kGrouped64 : kGrouped32;
+}
+
+const char *kernel_name(int kernel)
+{
+    switch (kernel) {
+    case kSkinny: return "weight-stream";
+    case kWide: return "wide 64x160";
+    case kStrip: return "strip 32x128";
+    case kTiled64x160: return "tiled 64x160";
+    case kTiled64x128: return "tiled 64x128";
+    case kTiled64x64: return "tiled 64x64";
+    case kTiled64x32: return "tiled 64x32";
+    case kTiled16x64: return "tiled 16x64";
+    case kTiled16x32: return "tiled 16x32";
+    case kSlot: return "expert-slot";
+    case kGrouped128: return "grouped 32x128";
+    case kGrouped64: return "grouped 32x64";
+    case kGrouped32: return "grouped 32x32";
+    default: return "none";
+    }
+}
+
+hipError_t launch_gemm(const GemmProblem &p, hipStream_t stream)
+{
+    const int kernel = plan_gemm(p);
+    if (kernel == kNoKernel)
+        return hipSuccess;
+    if (kernel == kSkinny)
         return launch_skinny(p, stream);
-    return p.act_bits == 4 ? launch_dense_bits<4>(p, stream) : launch_dense_bits<8>(p, stream);
+    return p.act_bits == 4 ? launch_dense_bits<4>(kernel, p, stream)
+                           : launch_dense_bits<8>(kernel, p, stream);
 }
 
 hipError_t launch_grouped_gemm(const GemmProblem &p, hipStream_t stream)
 {
-    if (p.rows == 0)
+    const int kernel = plan_grouped_gemm(p);
+    if (kernel == kNoKernel)
         return hipSuccess;
-    if (grouped_wide_fits(p))
+    if (kernel == kSlot)
         return launch_grouped_wide(p, stream);
-    return p.act_bits == 4 ? launch_grouped_bits<4>(p, stream) : launch_grouped_bits<8>(p, stream);
+    return p.act_bits == 4 ? launch_grouped_bits<4>(kernel, p, stream)
+                           : launch_grouped_bits<8>(kernel, p, stream);
 }
 
 hipError_t launch_blocksums(const GemmProblem &p, hipStream_t stream)

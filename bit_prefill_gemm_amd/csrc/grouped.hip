@@ -31,9 +31,9 @@
 //   - rows read through an optional row index (the gathered product), looked
 //     up one item ahead so that the index loads are in flight during the
 //     current item's stages.
-// The partial sums of the four K waves are added through LDS in a fixed order,
-// (w0 + w2) + (w1 + w3), so the result is bit-identical from run to run and
-// to the same product on explicitly permuted rows.
+// Every output is one wave's in-order accumulation over the blocks of K (no
+// partial sums are added across waves), so the result is bit-identical from
+// run to run and to the same product on explicitly permuted rows.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 

@@ -48,6 +48,29 @@ struct GemmProblem {
     int64_t m0, m1, n0, n1, expert;
 };
 
+// The kernels a product can run.  plan_gemm / plan_grouped_gemm name the one
+// launch_gemm / launch_grouped_gemm launch for a problem (host-only, from the
+// shape and code width); kernel_name gives its printable name.
+enum Kernel {
+    kNoKernel = 0,
+    kSkinny,       // weight-stream kernel, M <= 32 (skinny.hip)
+    kWide,         // 64 x 160 direct-load tiles, 4-bit (wide.hip)
+    kStrip,        // 32 x 128 strips (strip.hip)
+    kTiled64x160,  // tiled kernel shapes (gemm.hip)
+    kTiled64x128,
+    kTiled64x64,
+    kTiled64x32,
+    kTiled16x64,
+    kTiled16x32,
+    kSlot,         // grouped, 64-row expert slots, 4-bit (grouped.hip)
+    kGrouped128,   // grouped tiled kernel, 32-row slots (gemm.hip)
+    kGrouped64,
+    kGrouped32,
+};
+int plan_gemm(const GemmProblem &p);
+int plan_grouped_gemm(const GemmProblem &p);
+const char *kernel_name(int kernel);
+
 hipError_t launch_gemm(const GemmProblem &p, hipStream_t stream);
 // The weight-stream kernel for a few rows (dense only): usable when
 // skinny_fits(p).

@@ -359,18 +359,43 @@ bpg_status moe_combine(const float *dn, int64_t lddn, int64_t rows, const int32_
 
 /*
  * Parity and debug: the exact int32 block dot products
- * S[m][n][b] = sum_i q_a[m][32b+i] * (u[n][32b+i] - 8), computed by the same
- * matrix-instruction main loop as w4a4_gemm, for rows [m0, m1) and columns
- * [n0, n1) of expert `expert` (0 for a dense image).
+ * S[m][n][b] = sum_i q_a[m][32b+i] * (u[n][32b+i] - 8) ("509 tokens a second
+ * of prompt: the Hadamard route ships", section "Why prompts are a
+ * matrix-unit problem": the product is integer matrix work over Q4_0 codes),
+ * for rows [m0, m1) and columns [n0, n1) of expert `expert` (0 for a dense
+ * image).  This call always runs one kernel: the tiled kernel's 32 x 32
+ * matrix-instruction main loop (one v_mfma_i32_32x32x32_i8 per tile and
+ * block, the operand widening shared with every product kernel), writing S
+ * instead of applying the scales.  The kernels w4a4_gemm and
+ * w4a4_grouped_gemm route to (see w4a4_gemm_kernel_name) do not write S;
+ * their block sums are shown exact through their outputs: with power-of-two
+ * scales every step of the fp32 epilogue is exact, and with the activation
+ * scales of all blocks but one set to 0 the output is dw * S of that block.
  *
  *   scales  not read (may be NULL)
  *   sums    device, int32 [(m1-m0)][(n1-n0)][k/32]
+ *   expert  in [0, w->num_experts)
  * Errors: NULL, SHAPE, ALIGN, DTYPE, STAMP, DEVICE, LAUNCH.
  */
 bpg_status w4a4_gemm_blocksums(const void *codes, const float *scales, int act_bits, int64_t m,
                                const bpg_weights_desc *w, const void *w_dev, int64_t expert,
                                int64_t m0, int64_t m1, int64_t n0, int64_t n1, int32_t *sums,
                                void *stream);
+
+/*
+ * Routing queries, host only (no GPU call): the name of the kernel that
+ * w4a4_gemm (and its _bf16, _unrotated and _rot forms) with these arguments
+ * launches, and the same for w4a4_grouped_gemm (src_rows = 0) or
+ * w4a4_grouped_gemm_gather (src_rows = the activation rows it reads).  The
+ * kernel is chosen from the shape and the code width alone, so the answer is
+ * what the product call runs: "weight-stream", "wide 64x160",
+ * "strip 32x128", "tiled BMxBN", "expert-slot" or "grouped 32xBN"; "none"
+ * when there are no rows.  NULL for an invalid stamp or act_bits (static
+ * strings; the caller frees nothing).
+ */
+const char *w4a4_gemm_kernel_name(int act_bits, int64_t m, const bpg_weights_desc *w);
+const char *w4a4_grouped_gemm_kernel_name(int act_bits, int64_t total_rows, int64_t src_rows,
+                                          const bpg_weights_desc *w);
 
 #ifdef __cplusplus
 }

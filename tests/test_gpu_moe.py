@@ -14,12 +14,12 @@ import oracle
 from bit_prefill_gemm_amd import binding as bb
 from bit_prefill_gemm_amd import synth
 
-from gpu_util import act_to_device, oracle_codes, row_rel_err, sample_rows, torch_mod
+from gpu_util import (act_to_device, assert_within_bound, check_grouped_rows, oracle_codes,
+                      row_rel_err, sample_rows, torch_mod)
 
 pytestmark = pytest.mark.gpu
 
 TOL = 1e-3
-TIGHT = 2e-5
 
 
 @pytest.fixture(scope="module")
@@ -96,11 +96,8 @@ def test_gathered_grouped_gemm(torch, tokens, topk, experts, n, k, bits):
     rows_total = tokens * topk
     rows = sample_rows(rows_total, 24, seed=k)
     rt_np = row_token.cpu().numpy()
-    rr, cc = np.meshgrid(rows, np.arange(n), indexing="ij")
-    ref = oracle.grouped_points(q[rt_np], d[rt_np], off.cpu().numpy(), wq, dwq, rr.ravel(),
-                                cc.ravel()).reshape(len(rows), n)
-    err = row_rel_err(y.cpu().numpy()[rows], ref)
-    assert err <= TOL and err <= TIGHT, err
+    check_grouped_rows(y.cpu().numpy()[rows], q[rt_np], d[rt_np], off.cpu().numpy(), wq, dwq,
+                       rows, k, "gather", TOL)
 
 
 def swiglu_and_check(gu_np, inter, bits):
@@ -187,18 +184,14 @@ def test_expert_layer_stage_by_stage(torch):
     rows = sample_rows(T * K8, 12, seed=3)
     rt = row_token.cpu().numpy()
     off_np = off.cpu().numpy()
-    rr, cc = np.meshgrid(rows, np.arange(2 * I), indexing="ij")
-    ref = oracle.grouped_points(q[rt], d[rt], off_np, wq_gu, dw_gu, rr.ravel(),
-                                cc.ravel()).reshape(len(rows), 2 * I)
-    assert row_rel_err(gu.cpu().numpy()[rows], ref) <= TIGHT
+    check_grouped_rows(gu.cpu().numpy()[rows], q[rt], d[rt], off_np, wq_gu, dw_gu, rows, H,
+                       "layer gate/up", TOL)
     print("layer: swiglu", flush=True)
     hc, hs, hq, hd = swiglu_and_check(gu.cpu().numpy(), I, 4)
     print("layer: down", flush=True)
     dn = bb.w4a4_grouped_gemm(hc, hs, 4, off, Wdn)
     torch.cuda.synchronize()
-    rr, cc = np.meshgrid(rows, np.arange(H), indexing="ij")
-    ref = oracle.grouped_points(hq, hd, off_np, wq_dn, dw_dn, rr.ravel(),
-                                cc.ravel()).reshape(len(rows), H)
-    assert row_rel_err(dn.cpu().numpy()[rows], ref) <= TIGHT
+    check_grouped_rows(dn.cpu().numpy()[rows], hq, hd, off_np, wq_dn, dw_dn, rows, I,
+                       "layer down", TOL)
     print("layer: combine", flush=True)
     combine_and_check(dn.cpu().numpy(), slot_of.cpu().numpy(), w, T, K8)

@@ -1,8 +1,10 @@
 """GPU parity: the HIP path, called through the C ABI, against the CPU oracle.
 
 Bar: activation codes, scales and int32 block sums bit-exact; fp32 outputs
-within 1e-3 of the oracle's fp64 output in row-L2 relative error (and, as a
-tighter regression check, within the fp32 accumulation error).
+within 1e-3 of the oracle's fp64 output in row-L2 relative error, and every
+element within the fp32 accumulation bound (B + 8) * 2^-24 * sum_b |da dw S|.
+The block sums of the kernels the products route to are shown exact through
+their outputs in test_gpu_exact.py.
 """
 import numpy as np
 import pytest
@@ -11,13 +13,12 @@ import oracle
 from bit_prefill_gemm_amd import binding as bb
 from bit_prefill_gemm_amd import synth
 
-from gpu_util import (act_to_device, oracle_codes, rects, row_rel_err, sample_rows,
-                      torch_mod, weights_to_device)
+from gpu_util import (act_to_device, assert_within_bound, quantize_and_check, rects,
+                      row_rel_err, sample_rows, torch_mod, weights_to_device)
 
 pytestmark = pytest.mark.gpu
 
 TOL = 1e-3        # row-L2 relative error, the contract
-TIGHT = 2e-5      # fp32 accumulation over up to 544 blocks sits far below this
 
 
 @pytest.fixture(scope="module")
@@ -26,22 +27,6 @@ def torch():
     if not t.cuda.is_available():
         pytest.skip("no GPU")
     return t
-
-
-def quantize_and_check(x, bits, rotate_ref=True):
-    """Quantize on the GPU, compare codes and scales bit-exactly, return device + oracle codes."""
-    torch = torch_mod()
-    xd = act_to_device(x)
-    codes, scales = bb.quantize_act_h32(xd, bits)
-    torch.cuda.synchronize()
-    q, d, _ = oracle.quantize(x, bits)
-    got_codes = codes.cpu().numpy()
-    got_scales = scales.cpu().numpy()
-    exp_codes = oracle_codes(q, bits)
-    bad = np.argwhere(got_codes != exp_codes)
-    assert bad.size == 0, "codes differ at %s (of %d)" % (bad[:5].tolist(), len(bad))
-    assert np.array_equal(got_scales.view(np.uint32), d.view(np.uint32)), "scales differ"
-    return codes, scales, q, d
 
 
 # ------------------------------------------------------------------ quantizer
@@ -131,21 +116,32 @@ def test_blocksums_ffn_down_sampled(torch):
 
 # ------------------------------------------------------------------ dense GEMM
 
+def oracle_rows(q, d, w, dw, rows, n):
+    """The oracle's output and magnitude sums on `rows` (None: every row), all columns."""
+    if rows is None:
+        m = q.shape[0]
+        return (oracle.gemm_rect(q, d, w, dw, 0, m, 0, n),
+                oracle.gemm_abs_rect(q, d, w, dw, 0, m, 0, n))
+    ref = np.concatenate([oracle.gemm_rect(q, d, w, dw, r, r + 1, 0, n) for r in rows])
+    a = np.concatenate([oracle.gemm_abs_rect(q, d, w, dw, r, r + 1, 0, n) for r in rows])
+    return ref, a
+
+
 def check_gemm(x, blocks, n, k, bits, rows=None, label=""):
+    """The product of the workload through w4a4_gemm, on `rows` (None: all)."""
     torch = torch_mod()
     codes, scales, q, d = quantize_and_check(x, bits)
     W = weights_to_device(blocks, n, k)
-    print("gemm", label, x.shape, n, bits, flush=True)
+    print("gemm", label, x.shape, n, bits, bb.w4a4_gemm_kernel_name(bits, x.shape[0], W),
+          flush=True)
     y = bb.w4a4_gemm(codes, scales, bits, W)
     torch.cuda.synchronize()
     w, dw = oracle.q4_0_decode(blocks, k)
-    m = x.shape[0]
-    rows = np.arange(m) if rows is None else rows
-    yg = y.cpu().numpy()[rows]
-    ref = np.concatenate([oracle.gemm_rect(q, d, w, dw, r, r + 1, 0, n) for r in rows])
+    yg = y.cpu().numpy() if rows is None else y.cpu().numpy()[rows]
+    ref, a = oracle_rows(q, d, w, dw, rows, n)
     err = row_rel_err(yg, ref)
     assert err <= TOL, err
-    assert err <= TIGHT, err
+    assert_within_bound(yg, ref, a, k, label)
     return y, err
 
 
@@ -225,8 +221,8 @@ def test_gemm_few_rows_output_stride(torch):
     yb = ybig.cpu().numpy()
     assert np.all(yb[:, :8] == -1.0) and np.all(yb[:, 104:] == -1.0)
     w, dw = oracle.q4_0_decode(case["w"], 160)
-    ref = oracle.gemm_rect(q, d, w, dw, 0, 20, 0, 96)
-    assert row_rel_err(yb[:, 8:104], ref) <= TIGHT
+    ref, a = oracle_rows(q, d, w, dw, None, 96)
+    assert_within_bound(yb[:, 8:104], ref, a, 160, "few rows, strided")
 
 
 def test_gemm_m0_is_noop(torch):
@@ -251,8 +247,8 @@ def test_gemm_output_stride(torch):
     yb = ybig.cpu().numpy()
     assert np.all(yb[:, :4] == -1.0) and np.all(yb[:, 68:] == -1.0)
     w, dw = oracle.q4_0_decode(case["w"], 128)
-    ref = oracle.gemm_rect(q, d, w, dw, 0, 40, 0, 64)
-    assert row_rel_err(yb[:, 4:68], ref) <= TIGHT
+    ref, a = oracle_rows(q, d, w, dw, None, 64)
+    assert_within_bound(yb[:, 4:68], ref, a, 128, "strided")
 
 
 @pytest.mark.parametrize("m,k,n,bits", [(200, 1056, 10240, 4),   # wide kernel
@@ -275,24 +271,26 @@ def test_gemm_output_stride_wide_shapes(torch, m, k, n, bits):
     assert np.all(yb[:, :8] == -1.0) and np.all(yb[:, 8 + n:] == -1.0)
     w, dw = oracle.q4_0_decode(case["w"], k)
     rows = sample_rows(m, 8, seed=m)
-    ref = np.concatenate([oracle.gemm_rect(q, d, w, dw, r, r + 1, 0, n) for r in rows])
-    assert row_rel_err(yb[rows, 8:8 + n], ref) <= TIGHT
+    ref, a = oracle_rows(q, d, w, dw, rows, n)
+    assert_within_bound(yb[rows, 8:8 + n], ref, a, k, "strided")
 
 
 @pytest.mark.parametrize("bits", [4, 8])
 def test_gemm_attn512_full_size(torch, bits):
     """The benchmarked workload, in the benchmarked launch configuration."""
     t = synth.make("attn512")
-    check_gemm(t["x"], t["w"], 5120, 5120, bits, rows=sample_rows(512, 24, seed=bits),
-               label="attn512")
+    check_gemm(t["x"], t["w"], 5120, 5120, bits, label="attn512")
 
 
-def test_gemm_ffn512_full_size(torch):
+@pytest.mark.parametrize("bits", [4, 8])
+def test_gemm_ffn512_full_size(torch, bits):
+    """Every output of the FFN pair (the up projection on sampled rows: it runs
+    the gate's kernel on other weights)."""
     t = synth.make("ffn512")
-    rows = sample_rows(512, 8, seed=3)
-    check_gemm(t["x1"], t["w_gate"], 17408, 5120, 4, rows=rows, label="ffn gate")
-    check_gemm(t["x1"], t["w_up"], 17408, 5120, 4, rows=rows, label="ffn up")
-    check_gemm(t["x2"], t["w_down"], 5120, 17408, 4, rows=rows, label="ffn down")
+    check_gemm(t["x1"], t["w_gate"], 17408, 5120, bits, label="ffn gate")
+    check_gemm(t["x1"], t["w_up"], 17408, 5120, bits, rows=sample_rows(512, 8, seed=3),
+               label="ffn up")
+    check_gemm(t["x2"], t["w_down"], 5120, 17408, bits, label="ffn down")
 
 
 @pytest.mark.parametrize("name,bits", [("m16_gate", 4), ("m16_down", 4), ("m16_attn", 4),
@@ -304,7 +302,8 @@ def test_gemm_m16_full_size(torch, name, bits):
 
 
 def test_long1024_routes_and_error_vs_unquantized(torch):
-    """Both routes match the oracle; report their error against the fp64 unquantized product."""
+    """Both routes match the oracle on every output; report their error
+    against the fp64 unquantized product (on sampled rows)."""
     t = synth.make("long1024")
     rows = sample_rows(1024, 6, seed=4)
     cols = np.arange(17408)
@@ -313,7 +312,7 @@ def test_long1024_routes_and_error_vs_unquantized(torch):
     ref = oracle.ref_points(t["x"], w, dw, rr.ravel(), cc.ravel()).reshape(len(rows), -1)
     errs = {}
     for bits in (4, 8):
-        y, _ = check_gemm(t["x"], t["w"], 17408, 5120, bits, rows=rows, label="long1024")
+        y, _ = check_gemm(t["x"], t["w"], 17408, 5120, bits, label="long1024")
         errs[bits] = row_rel_err(y.cpu().numpy()[rows], ref)
     print("error vs fp64 unquantized: int4 %.4g, q8 %.4g" % (errs[4], errs[8]))
     assert errs[8] < errs[4] < 0.5
@@ -338,9 +337,12 @@ def check_grouped(x, blocks, offsets, n, k, E, bits, rows=None, label=""):
     rr, cc = np.meshgrid(rows, np.arange(n), indexing="ij")
     ref = oracle.grouped_points(q, d, offsets, wq, dwq, rr.ravel(), cc.ravel()).reshape(
         len(rows), n)
+    a = oracle.grouped_abs_points(q, d, offsets, wq, dwq, rr.ravel(), cc.ravel()).reshape(
+        len(rows), n)
     yg = y.cpu().numpy()[rows]
     err = row_rel_err(yg, ref)
-    assert err <= TOL and err <= TIGHT, err
+    assert err <= TOL, err
+    assert_within_bound(yg, ref, a, k, label)
     return y, codes, scales, q, W, wq
 
 

@@ -25,4 +25,17 @@ def test_hash_is_stable_and_covers_the_kernels():
     h = bench.source_hash()
     assert len(h) == 16 and h == bench.source_hash()
     names = {os.path.basename(f) for f in bench.GEMM_SRCS}
-    assert {"gemm.hip", "wide.hip", "strip.hip", "grouped.hip", "skinny.hip"} <= names
+    assert {"gemm.hip", "wide.hip", "strip.hip", "grouped.hip", "skinny.hip", "operands.h",
+            "internal.h"} <= names
+
+
+def test_hash_covers_the_compile_flags(monkeypatch):
+    """A change of the code-generation flags changes the hash (so counters
+    taken with other flags are not reported as current); include paths,
+    which differ between checkouts, are not part of them."""
+    from bit_prefill_gemm_amd import build
+    h = bench.source_hash()
+    assert not any(f.startswith("/") for f in build.KERNEL_FLAGS)
+    assert set(build.KERNEL_FLAGS) <= set(build.FLAGS)
+    monkeypatch.setattr(build, "KERNEL_FLAGS", build.KERNEL_FLAGS + ["-O2"])
+    assert bench.source_hash() != h
