@@ -37,6 +37,7 @@ namespace bpg {
 namespace {
 
 constexpr int kThreads = 256;           // 64 blocks of 32 values per workgroup
+constexpr int kQuantRounds = 1;         // rounds of 16 blocks per wave (more rounds measured slower)
 constexpr int kQuadXor1 = 0xB1;         // DPP quad_perm [1,0,3,2]
 constexpr int kQuadXor2 = 0x4E;         // DPP quad_perm [2,3,0,1]
 
@@ -197,38 +198,202 @@ __device__ __forceinline__ void quantize_block(float (&v)[8], int t, int rot, in
         scales[row * nb + b] = d;
 }
 
-// One quad of lanes per 32-block, grid-stride over the blocks of the matrix;
-// the next block's values are loaded before the current block's arithmetic.
-// All four lanes of a quad walk the same blocks and leave the loop together,
-// so the quad-local DPP exchanges never read an exited lane.
-template <typename T, int BITS>
-__global__ __launch_bounds__(kThreads) void quantize_h32_kernel(
-    const T *__restrict__ x, int64_t k, int64_t ldx, int64_t nblk_total, int rot,
+// The rotation of one block (span ROT = 0: none, 32, 64, 128): lane t holds
+// elements {4t..4t+3} and {16+4t..16+4t+3} (v[0..3], v[4..7]); h = 1, 2
+// inside the lane, h = 4 with lane t^1, h = 8 with t^2 (the lane with the
+// bit clear is lower), h = 16 inside the lane (v[i] with v[i+4]), h = 32, 64
+// with the adjacent quads of a longer span; then times fp32(1/sqrt(ROT)).
+template <int ROT>
+__device__ __forceinline__ void rotate_p(float (&v)[8], int t, int lane)
+{
+    if constexpr (ROT != 0) {
+#pragma unroll
+        for (int base = 0; base < 8; base += 4) {
+            const float a0 = v[base], a1 = v[base + 1], a2 = v[base + 2], a3 = v[base + 3];
+            v[base] = a0 + a1;
+            v[base + 1] = a0 - a1;
+            v[base + 2] = a2 + a3;
+            v[base + 3] = a2 - a3;
+        }
+#pragma unroll
+        for (int base = 0; base < 8; base += 4) {
+            const float a0 = v[base], a1 = v[base + 1], a2 = v[base + 2], a3 = v[base + 3];
+            v[base] = a0 + a2;
+            v[base + 2] = a0 - a2;
+            v[base + 1] = a1 + a3;
+            v[base + 3] = a1 - a3;
+        }
+        cross_stage<kQuadXor1>(v, (t & 1) != 0);
+        cross_stage<kQuadXor2>(v, (t & 2) != 0);
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const float a = v[i], c = v[i + 4];
+            v[i] = a + c;
+            v[i + 4] = a - c;
+        }
+        if constexpr (ROT >= 64)
+            cross_quad_stage<kSwzXor4>(v, (lane & 4) != 0);
+        if constexpr (ROT >= 128)
+            cross_quad_stage<kSwzXor8>(v, (lane & 8) != 0);
+        const float c = ROT == 64 ? 0.125f
+                                  : __uint_as_float(ROT == 128 ? 0x3DB504F3u : 0x3E3504F3u);
+#pragma unroll
+        for (int i = 0; i < 8; i++)
+            v[i] = v[i] * c;
+    }
+}
+
+// R rounds of 16 blocks per wave, one quad per block, in phases over the
+// rounds (loads, rotations, block maxima, scales, codes, stores) so that the
+// rounds' dependency chains overlap.  Block b of row `row` of round r is
+// block 16 (R wave + r) + quad of the flattened matrix.  In the last wave,
+// quads past the end repeat the last block's arithmetic and store nothing
+// (a span never straddles the end, so every exchange between quads stays
+// between quads of the same kind).
+template <typename T, int BITS, int ROT, int R, typename I>
+__global__ __launch_bounds__(kThreads) void quantize_rows_kernel(
+    const T *__restrict__ x, int64_t k, int64_t ldx, int64_t nblk_total,
     uint8_t *__restrict__ codes, float *__restrict__ scales)
 {
-    const int t = threadIdx.x & 3;
-    const int64_t stride = (int64_t)gridDim.x * (kThreads / 4);
-    const int64_t nb = k / 32;
-    int64_t blk = (int64_t)blockIdx.x * (kThreads / 4) + (threadIdx.x >> 2);
-    if (blk >= nblk_total)
-        return;
-    float v[8];
-    int64_t row = blk / nb;
-    load8(x + row * ldx + (blk - row * nb) * 32, t, v);
-    while (true) {
-        const int64_t cur_row = row, cur_b = blk - row * nb;
-        const int64_t next = blk + stride;
-        float nv[8];
-        if (next < nblk_total) {
-            row = next / nb;
-            load8(x + row * ldx + (next - row * nb) * 32, t, nv);
+    const int lane = threadIdx.x & 63;
+    const int t = lane & 3, qd = lane >> 2;
+    const I nb = (I)(k / 32);
+    const I total = (I)nblk_total;
+    const I wave = (I)blockIdx.x * (kThreads / 64) +
+                   (I)__builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    I row[R], bk[R];
+    bool live[R];
+#pragma unroll
+    for (int r = 0; r < R; r++) {
+        const I first = wave * (16 * R) + 16 * r; // uniform
+        I blk = first + qd;
+        live[r] = blk < total;
+        blk = live[r] ? blk : total - 1;
+        if (sizeof(I) == 4 && nb >= 16 && first + 15 < total) {
+            // the division on the scalar unit: the quads' blocks are in the
+            // first block's row or the next
+            const I r0 = first / nb;
+            const I b0 = first - r0 * nb;
+            const I b = b0 + qd;
+            row[r] = b < nb ? r0 : r0 + 1;
+            bk[r] = b < nb ? b : b - nb;
+        } else {
+            row[r] = blk / nb;
+            bk[r] = blk - row[r] * nb;
         }
-        quantize_block<BITS>(v, t, rot, cur_row, cur_b, k, nb, codes, scales);
-        if (next >= nblk_total)
-            break;
-        blk = next;
+    }
+    float v[R][8];
+#pragma unroll
+    for (int r = 0; r < R; r++)
+        load8(x + (int64_t)row[r] * ldx + (int64_t)bk[r] * 32, t, v[r]);
+#pragma unroll
+    for (int r = 0; r < R; r++)
+        rotate_p<ROT>(v[r], t, lane);
+
+    constexpr float kQmax = BITS == 4 ? 7.0f : 127.0f;
+    constexpr float kQmin = BITS == 4 ? -8.0f : -127.0f;
+    float d[R];
+#pragma unroll
+    for (int r = 0; r < R; r++) {
+        float amax = 0.0f;
+#pragma unroll
         for (int i = 0; i < 8; i++)
-            v[i] = nv[i];
+            amax = fmaxf(amax, fabsf(v[r][i]));
+        amax = fmaxf(amax, quad_swap<kQuadXor1>(amax));
+        amax = fmaxf(amax, quad_swap<kQuadXor2>(amax));
+        // IEEE division; an all-zero block has scale 0
+        d[r] = amax / kQmax;
+    }
+    // rint(v / d) with the IEEE quotient, taken first as v * rcp(d): its
+    // error is below |v/d| * 3 * 2^-24 <= 2.3e-5 (|v/d| <= 127), so wherever
+    // that product lies at least 1e-4 from a half-integer it rounds to the
+    // same integer as the correctly rounded quotient.  The rare values within
+    // that band, and scales too small for the reciprocal, make the whole wave
+    // take the division (one uniform branch).
+    float qv[R][8];
+    bool slow = false;
+#pragma unroll
+    for (int r = 0; r < R; r++) {
+        const float rd = __builtin_amdgcn_rcpf(d[r]);
+        slow |= d[r] != 0.0f && !(d[r] >= 0x1p-100f);
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            qv[r][i] = v[r][i] * rd;
+            slow |= fabsf(fabsf(qv[r][i] - rintf(qv[r][i])) - 0.5f) < 1e-4f;
+        }
+    }
+    if (__builtin_amdgcn_ballot_w64(slow) != 0) {
+#pragma unroll
+        for (int r = 0; r < R; r++)
+#pragma unroll
+            for (int i = 0; i < 8; i++)
+                qv[r][i] = v[r][i] / d[r];
+    }
+    uint2 out[R];
+#pragma unroll
+    for (int r = 0; r < R; r++) {
+        int q[8];
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            const float c = d[r] != 0.0f ? rintf(qv[r][i]) : 0.0f;
+            q[i] = (int)fminf(fmaxf(c, kQmin), kQmax);
+        }
+        if constexpr (BITS == 4) {
+            // byte 4t+i = code(4t+i) low nibble | code(16+4t+i) high nibble
+            uint32_t word = 0;
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+                word |= (uint32_t)((q[i] & 0xF) | ((q[i + 4] & 0xF) << 4)) << (8 * i);
+            out[r].x = word;
+            out[r].y = 0;
+        } else {
+            out[r].x = out[r].y = 0;
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                out[r].x |= (uint32_t)(q[i] & 0xFF) << (8 * i);
+                out[r].y |= (uint32_t)(q[i + 4] & 0xFF) << (8 * i);
+            }
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < R; r++) {
+        if (!live[r])
+            continue;
+        if constexpr (BITS == 4) {
+            *reinterpret_cast<uint32_t *>(codes + (int64_t)row[r] * (k / 2) + (int64_t)bk[r] * 16 +
+                                          4 * t) = out[r].x;
+        } else {
+            uint8_t *dst = codes + (int64_t)row[r] * k + (int64_t)bk[r] * 32;
+            *reinterpret_cast<uint32_t *>(dst + 4 * t) = out[r].x;
+            *reinterpret_cast<uint32_t *>(dst + 16 + 4 * t) = out[r].y;
+        }
+        if (t == 0)
+            scales[(int64_t)row[r] * nb + bk[r]] = d[r];
+    }
+}
+
+template <typename T, int BITS, int ROT>
+void launch_rows(dim3 grid, const T *x, int64_t k, int64_t ldx, int64_t nblk, uint8_t *codes,
+                 float *scales, hipStream_t stream)
+{
+    constexpr int R = kQuantRounds;
+    if (nblk + 16 * R * kThreads < ((int64_t)1 << 31))
+        quantize_rows_kernel<T, BITS, ROT, R, uint32_t><<<grid, kThreads, 0, stream>>>(
+            x, k, ldx, nblk, codes, scales);
+    else
+        quantize_rows_kernel<T, BITS, ROT, R, int64_t><<<grid, kThreads, 0, stream>>>(
+            x, k, ldx, nblk, codes, scales);
+}
+
+template <typename T, int BITS>
+void launch_rows_rot(dim3 grid, const T *x, int64_t k, int64_t ldx, int64_t nblk, int rot,
+                     uint8_t *codes, float *scales, hipStream_t stream)
+{
+    switch (rot) {
+    case 0: launch_rows<T, BITS, 0>(grid, x, k, ldx, nblk, codes, scales, stream); break;
+    case 64: launch_rows<T, BITS, 64>(grid, x, k, ldx, nblk, codes, scales, stream); break;
+    case 128: launch_rows<T, BITS, 128>(grid, x, k, ldx, nblk, codes, scales, stream); break;
+    default: launch_rows<T, BITS, 32>(grid, x, k, ldx, nblk, codes, scales, stream); break;
     }
 }
 
@@ -316,22 +481,25 @@ hipError_t launch_quantize(const void *x, int dtype, int64_t m, int64_t k, int64
     const int64_t nblk = m * (k / 32);
     if (nblk == 0)
         return hipSuccess;
-    // enough quads to fill every CU several times over; each walks blocks
-    const int64_t needed = (nblk + kThreads / 4 - 1) / (kThreads / 4);
-    const dim3 grid((unsigned)(needed < 2048 ? needed : 2048));
+    constexpr int R = kQuantRounds;
+    const int64_t waves = (nblk + 16 * R - 1) / (16 * R);
+    const int64_t wgs = (waves + kThreads / 64 - 1) / (kThreads / 64);
+    if (wgs >= ((int64_t)1 << 31))
+        return hipErrorInvalidValue;
+    const dim3 grid((unsigned)wgs);
     uint8_t *c = static_cast<uint8_t *>(codes);
     if (dtype == 0 && act_bits == 4)
-        quantize_h32_kernel<float, 4><<<grid, kThreads, 0, stream>>>(
-            static_cast<const float *>(x), k, ldx, nblk, rot, c, scales);
+        launch_rows_rot<float, 4>(grid, static_cast<const float *>(x), k, ldx, nblk, rot, c, scales,
+                                  stream);
     else if (dtype == 0)
-        quantize_h32_kernel<float, 8><<<grid, kThreads, 0, stream>>>(
-            static_cast<const float *>(x), k, ldx, nblk, rot, c, scales);
+        launch_rows_rot<float, 8>(grid, static_cast<const float *>(x), k, ldx, nblk, rot, c, scales,
+                                  stream);
     else if (act_bits == 4)
-        quantize_h32_kernel<uint16_t, 4><<<grid, kThreads, 0, stream>>>(
-            static_cast<const uint16_t *>(x), k, ldx, nblk, rot, c, scales);
+        launch_rows_rot<uint16_t, 4>(grid, static_cast<const uint16_t *>(x), k, ldx, nblk, rot, c,
+                                     scales, stream);
     else
-        quantize_h32_kernel<uint16_t, 8><<<grid, kThreads, 0, stream>>>(
-            static_cast<const uint16_t *>(x), k, ldx, nblk, rot, c, scales);
+        launch_rows_rot<uint16_t, 8>(grid, static_cast<const uint16_t *>(x), k, ldx, nblk, rot, c,
+                                     scales, stream);
     return hipGetLastError();
 }
 
