@@ -14,12 +14,19 @@
 //     matrix operands for the group's four blocks; an activation read holds
 //     one block of one row and a 4x4 transpose across the lane rows (gfx950
 //     permlane swaps) turns four of them into the operands of four blocks;
-//   - operands go straight from global memory into registers (no LDS
-//     staging, no barriers in the main loop), with D groups of loads in
-//     flight per wave while a group is computed;
-//   - the few activation rows are re-read from L2; their scales are staged
-//     once per workgroup in LDS, transposed, so the epilogue reads four rows'
-//     scales with one LDS read;
+//   - weight operands go straight from global memory into registers (no
+//     barriers in the main loop), with D groups of loads in flight per wave
+//     while a group is computed;
+//   - the few activation rows are staged once per workgroup in LDS when they
+//     fit (16 rows of K <= 6144 4-bit codes): read with whole cache lines and
+//     stored with a padded row stride, so a wave's operand read of 16 rows
+//     hits 16 distinct bank groups.  Read from L2 with every group instead,
+//     each 16-lane quarter of an activation load touches 16 rows, i.e. 16
+//     separate lines for 256 bytes, and those requests slow the weight stream
+//     itself (measured: the rows from L2 cost a third more time than staged
+//     ones).  Larger K re-reads the rows from L2;
+//   - the row scales are staged once per workgroup in LDS, transposed, so the
+//     epilogue reads four rows' scales with one LDS read;
 //   - the partial sums of the waves are added in a fixed order (wave 0, 1,
 //     ...) through LDS, so the result is bit-identical from run to run.
 // The per-block arithmetic is the one of the tiled kernel: operands widened
@@ -37,14 +44,15 @@ namespace bpg {
 
 namespace {
 
-template <int BITS_, int TM_, int NW_, int TN_, int D_>
+template <int BITS_, int TM_, int NW_, int TN_, int D_, bool AL_>
 struct SkCfg {
     static constexpr int BITS = BITS_, TM = TM_, NW = NW_;
     static constexpr int TN = TN_;                    // 16-column tiles per workgroup: one image tile
     static_assert(TN == 2, "one 32-column image tile per workgroup");
     static constexpr int kCols = 16 * TN;
     // groups of four blocks in flight per wave: one when a wave walks many
-    // groups, two when it walks few.  Deeper rings measured slower: with every
+    // groups and reads its activation rows from L2, two otherwise.  Deeper
+    // rings measured slower, even for the weight stream alone: with every
     // wave of the grid streaming, more outstanding reads only lengthen the
     // memory queues (the waves of a SIMD still overlap one another's waits).
     static constexpr int D = D_;
@@ -55,6 +63,10 @@ struct SkCfg {
     static constexpr int kShift = BITS == 4 ? 8 : 4;  // log2 of the operand widening
     static constexpr int kR = TM * TN * 4;            // accumulators per lane
     static constexpr int kLdsRed = NW * kR * 64 * 4;  // bytes for the final reduction
+    // activation rows staged once per workgroup in LDS (row stride padded by
+    // 16 bytes, so that the 16 rows of an operand read fall in distinct banks)
+    // instead of being re-read from L2 with every group
+    static constexpr bool AL = AL_;
 };
 
 // The same address in every lane, made visibly uniform (scalar registers).
@@ -108,6 +120,9 @@ __global__ __launch_bounds__(C::kThreads) void skinny_kernel(GemmProblem p)
     const int64_t col0 = tile * C::kCols;
 
     float *Da = lds;
+    // staged activation rows (AL): row m at act_lds + m * a_stride bytes
+    const int a_stride = (int)(p.k * kAB / 32) + 16;
+    uint8_t *act_lds = reinterpret_cast<uint8_t *>(lds) + (size_t)4 * NG * kRows * 4;
 
     // ---- this wave's groups and its operand offsets.  Per group and lane:
     //      weights: one 16-byte read per 16-column tile = slot g of column c
@@ -136,7 +151,7 @@ __global__ __launch_bounds__(C::kThreads) void skinny_kernel(GemmProblem p)
     }
 
     // ring of D groups of operands in registers
-    uint4 rw[D][TN], ra[D][TM][kAH], rdw[D];
+    uint4 rw[D][TN], ra[C::AL ? 1 : D][TM][kAH], rdw[D];
     auto load = [&](int d, int G) {
         const gptr wb = w_base + G * 2304;
         // the last group may end past block B-1: those lanes re-read block B-1
@@ -145,11 +160,13 @@ __global__ __launch_bounds__(C::kThreads) void skinny_kernel(GemmProblem p)
         for (int j = 0; j < TN; j++)
             rw[d][j] = gload16(wb, vw[j]);
         rdw[d] = gload16(wb, vdw);
+        if constexpr (!C::AL) {
 #pragma unroll
-        for (int i = 0; i < TM; i++)
+            for (int i = 0; i < TM; i++)
 #pragma unroll
-            for (int h = 0; h < kAH; h++)
-                ra[d][i][h] = gload16(a_base, va[i] + bq * kAB + 16 * h);
+                for (int h = 0; h < kAH; h++)
+                    ra[d][i][h] = gload16(a_base, va[i] + bq * kAB + 16 * h);
+        }
     };
 
     float acc[TM][TN][4];
@@ -170,21 +187,32 @@ __global__ __launch_bounds__(C::kThreads) void skinny_kernel(GemmProblem p)
     // last group may hold blocks past B: the image gives them scale 0 and LDS
     // row scale 0, so they add exactly zero.
     auto compute = [&](int d, int G) {
+        const int ad = C::AL ? 0 : d; // the activation operands' slot
+        if constexpr (C::AL) {
+            // from the staged rows: block 4G+g of row c (blocks past B re-read B-1)
+            const int bq = min(4 * G + g, B - 1);
+#pragma unroll
+            for (int i = 0; i < TM; i++)
+#pragma unroll
+                for (int h = 0; h < kAH; h++)
+                    ra[0][i][h] = *reinterpret_cast<const uint4 *>(act_lds + (16 * i + c) * a_stride +
+                                                                   bq * kAB + 16 * h);
+        }
 #pragma unroll
         for (int i = 0; i < TM; i++)
 #pragma unroll
             for (int h = 0; h < kAH; h++)
-                transpose_rows4(ra[d][i][h]);
+                transpose_rows4(ra[ad][i][h]);
         v4i s[4][TN][TM];
 #pragma unroll
         for (int q = 0; q < 4; q++) {
             long a[TM];
 #pragma unroll
             for (int i = 0; i < TM; i++) {
-                const uint32_t lo = q == 0 ? ra[d][i][0].x : q == 1 ? ra[d][i][0].y
-                                  : q == 2 ? ra[d][i][0].z : ra[d][i][0].w;
-                const uint32_t hi = q == 0 ? ra[d][i][kAH - 1].x : q == 1 ? ra[d][i][kAH - 1].y
-                                  : q == 2 ? ra[d][i][kAH - 1].z : ra[d][i][kAH - 1].w;
+                const uint32_t lo = q == 0 ? ra[ad][i][0].x : q == 1 ? ra[ad][i][0].y
+                                  : q == 2 ? ra[ad][i][0].z : ra[ad][i][0].w;
+                const uint32_t hi = q == 0 ? ra[ad][i][kAH - 1].x : q == 1 ? ra[ad][i][kAH - 1].y
+                                  : q == 2 ? ra[ad][i][kAH - 1].z : ra[ad][i][kAH - 1].w;
                 // 4-bit: low and high nibbles of dword g; 8-bit: bytes 4g.. and 16+4g..
                 a[i] = kAH == 1 ? pack2(act_lo(lo), act_hi(lo)) : pack2(lo, hi);
             }
@@ -247,7 +275,25 @@ __global__ __launch_bounds__(C::kThreads) void skinny_kernel(GemmProblem p)
             for (int m = 0; m < kRows; m++)
                 Da[b * kRows + m] = dv[m];
     };
+    // activation rows (AL): thread t copies 16-byte chunks t, t + NT, ... of
+    // every row (rows past M repeat the last row), full cache lines per wave
+    const int cpr = (int)(p.k * kAB / 32 / 16); // 16-byte chunks per row
+    uint4 av[C::AL ? kRows : 1];
+    auto act_load = [&](int ch) {
+        if (ch < cpr)
+#pragma unroll
+            for (int m = 0; m < kRows; m++)
+                av[m] = gload16(a_base, (uint32_t)((m < rows ? m : rows - 1) * arow) + (uint32_t)ch * 16u);
+    };
+    auto act_store = [&](int ch) {
+        if (ch < cpr)
+#pragma unroll
+            for (int m = 0; m < kRows; m++)
+                *reinterpret_cast<uint4 *>(act_lds + m * a_stride + ch * 16) = av[m];
+    };
     da_load(tid);
+    if constexpr (C::AL)
+        act_load(tid);
     __builtin_amdgcn_sched_barrier(0);
 
     // The wave walks its groups starting at an offset that depends on the
@@ -271,6 +317,13 @@ __global__ __launch_bounds__(C::kThreads) void skinny_kernel(GemmProblem p)
     for (int b = tid + NT; b < da_cols; b += NT) {
         da_load(b);
         da_store(b);
+    }
+    if constexpr (C::AL) {
+        act_store(tid);
+        for (int ch = tid + NT; ch < cpr; ch += NT) {
+            act_load(ch);
+            act_store(ch);
+        }
     }
     __syncthreads(); // the scales in LDS
 
@@ -312,8 +365,10 @@ __global__ __launch_bounds__(C::kThreads) void skinny_kernel(GemmProblem p)
 template <class C>
 size_t skinny_lds(const GemmProblem &p)
 {
-    const size_t da = (size_t)((p.k / 32 + 3) / 4) * 4 * C::kRows * 4;
-    return da > (size_t)C::kLdsRed ? da : (size_t)C::kLdsRed;
+    size_t bytes = (size_t)((p.k / 32 + 3) / 4) * 4 * C::kRows * 4;
+    if (C::AL)
+        bytes += (size_t)C::kRows * (size_t)(p.k * C::kAB / 32 + 16);
+    return bytes > (size_t)C::kLdsRed ? bytes : (size_t)C::kLdsRed;
 }
 
 template <class C>
@@ -324,18 +379,38 @@ hipError_t launch_cfg(const GemmProblem &p, hipStream_t stream)
     return hipGetLastError();
 }
 
-// Waves per workgroup: enough waves in the whole grid to keep the weight
-// stream busy (about 8 per CU), each with at least 4 groups of K.
-template <int BITS, int TM, int TN, int D>
+template <int BITS, int TM, int TN, int D, bool AL>
 hipError_t launch_nw(const GemmProblem &p, int nw, hipStream_t stream)
 {
     if (nw == 4)
-        return launch_cfg<SkCfg<BITS, TM, 4, TN, D>>(p, stream);
+        return launch_cfg<SkCfg<BITS, TM, 4, TN, D, AL>>(p, stream);
     if constexpr (TM == 1) {
         if (nw == 16)
-            return launch_cfg<SkCfg<BITS, TM, 16, TN, D>>(p, stream);
+            return launch_cfg<SkCfg<BITS, TM, 16, TN, D, AL>>(p, stream);
     }
-    return launch_cfg<SkCfg<BITS, TM, 8, TN, D>>(p, stream);
+    return launch_cfg<SkCfg<BITS, TM, 8, TN, D, AL>>(p, stream);
+}
+
+// Activation rows staged in LDS: one row tile whose rows and transposed
+// scales fit the 64 KB of dynamic LDS.
+template <int TM>
+bool stage_rows(const GemmProblem &p)
+{
+    if (TM != 1)
+        return false;
+    const int64_t da = (p.k / 32 + 3) / 4 * 4 * 16 * 4;
+    const int64_t rows = 16 * (p.k * (p.act_bits == 4 ? 16 : 32) / 32 + 16);
+    return da + rows <= 65536;
+}
+
+template <int BITS, int TM, int TN, int D>
+hipError_t launch_al(const GemmProblem &p, int nw, hipStream_t stream)
+{
+    if constexpr (TM == 1) {
+        if (stage_rows<TM>(p))
+            return launch_nw<BITS, TM, TN, D, true>(p, nw, stream);
+    }
+    return launch_nw<BITS, TM, TN, D, false>(p, nw, stream);
 }
 
 // Waves per workgroup: enough waves in the whole grid to keep the weight
@@ -349,9 +424,11 @@ hipError_t launch_tn(const GemmProblem &p, hipStream_t stream)
     int nw = 4;
     while (nw < nw_max && tiles * nw < 2048 && NG / (2 * nw) >= 4)
         nw *= 2;
-    if (NG / nw <= 6)
-        return launch_nw<BITS, TM, TN, 2>(p, nw, stream);
-    return launch_nw<BITS, TM, TN, 1>(p, nw, stream);
+    // two groups in flight with staged rows (the operand loads are the weights
+    // alone) or with few groups per wave; one otherwise
+    if (NG / nw <= 6 || stage_rows<TM>(p))
+        return launch_al<BITS, TM, TN, 2>(p, nw, stream);
+    return launch_nw<BITS, TM, TN, 1, false>(p, nw, stream);
 }
 
 template <int BITS, int TM>
