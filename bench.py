@@ -19,8 +19,10 @@ weighted combine; `kernel_us` gives each kernel's own duration).
 
 Prints ONE JSON line.  `value` is prompt tokens per second of the step.  The
 `roofline` object covers the GEMM kernel (the dominant kernel).  Its average
-duration is measured with HIP events recorded on the launch stream around
-every 8th GEMM of the timed region.  The bound is whichever algorithmic floor
+duration is measured with HIP events recorded on the launch stream around a
+graph replay of 40 back-to-back GEMM launches over the same cold copies,
+right after the timed steps (an event pair around each single launch would
+add its two queue packets to every launch).  The bound is whichever algorithmic floor
 of the contraction is larger: its 2*M*N*K integer ops at the dense int8
 matrix peak ("mfma"), or its HBM bytes at the HBM peak ("hbm": a few rows, and
 the grouped expert GEMMs, whose weight stream is larger).  `epilogue_valu`
@@ -28,8 +30,9 @@ gives the same launch against the other floor this method has on gfx950: the
 fp32 epilogue (two FMAs per output element and 32-block) at the fp32 vector
 peak.
 `traffic` comes from the committed rocprofv3 counter summary for this kernel
-and workload, and is null if the kernel source or its compile flags changed
-since it was taken.
+and workload, and is null if that kernel's sources (its own file and the
+shared routing and operand code) or the compile flags changed since it was
+taken.
 `configs` (default workload only) measures every other workload in the same
 run, with fewer steps and no CPU baseline: GEMM time, kernel, roofline
 fraction and tokens/s of each.
@@ -85,17 +88,51 @@ WORKLOADS = {
 }
 # kernel sources of the GEMM paths (the tiled, wide, strip and grouped kernels,
 # the weight-stream kernel used for a few rows, and the headers they share)
-GEMM_SRCS = [os.path.join(ROOT, "bit_prefill_gemm_amd", "csrc", f)
+_CSRC = os.path.join(ROOT, "bit_prefill_gemm_amd", "csrc")
+GEMM_SRCS = [os.path.join(_CSRC, f)
              for f in ("gemm.hip", "skinny.hip", "wide.hip", "strip.hip", "grouped.hip",
                        "operands.h", "internal.h")]
+# what every GEMM launch depends on (routing, the tiled kernel, shared operand
+# code) and, by the kernel name the routing query returns, its own source
+SHARED_SRCS = [os.path.join(_CSRC, f) for f in ("gemm.hip", "operands.h", "internal.h")]
+KERNEL_SRC = {"weight-stream": "skinny.hip", "wide": "wide.hip", "strip": "strip.hip",
+              "expert-slot": "grouped.hip", "grouped": "grouped.hip", "tiled": "gemm.hip"}
 # the workloads measured beside the default one (name, activation bits)
 CONFIG_RUNS = [("attn512", 8), ("ffn512_gate", 4), ("ffn512_down", 4), ("ffn512_gate", 8),
                ("ffn512_down", 8), ("long1024", 4), ("long1024", 8), ("moe512_gu", 4),
                ("moe512_dn", 4), ("moe512_layer", 4), ("m16_gate", 4), ("m16_down", 4),
                ("m16_attn", 4)]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_traffic.json")
-# timed steps between two whose GEMM is bracketed by events
-EVENT_EVERY = 8
+GRAPH_LAUNCHES = 40   # launches per captured graph when a kernel is timed alone
+GRAPH_REPLAYS = 5
+
+
+def graph_time_us(torch, stream, launch, n=GRAPH_LAUNCHES, replays=GRAPH_REPLAYS):
+    """Per-launch duration of launch(0), ..., launch(n-1) on `stream`, replayed
+    from one captured graph: the kernels run back to back with no host work and
+    no event packets between them, so the time between the two events around a
+    replay, divided by n, is one kernel's duration plus one dispatch gap.  (An
+    event pair around each launch instead adds the cost of its two packets to
+    every launch, several microseconds, which dominates a short kernel.)  The
+    median over `replays` replays after one untimed replay."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for i in range(n):
+            launch(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ts = []
+    with torch.cuda.stream(stream):
+        g.replay()
+        for _ in range(replays):
+            e0.record(stream)
+            g.replay()
+            e1.record(stream)
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e3 / n)
+    torch.cuda.synchronize()
+    del g
+    return float(np.median(ts))
 
 
 def parse():
@@ -149,12 +186,24 @@ def strip_comments(text):
     return " ".join("".join(out).split())
 
 
-def source_hash():
-    """First 16 hex digits of sha256 over the GEMM kernel sources (comments
-    removed) and the flags they are compiled with."""
+def kernel_srcs(kname=None):
+    """The sources one routed kernel depends on (kname as the routing query
+    names it, e.g. "wide 64x160"), or every GEMM source (kname None)."""
+    if kname is None:
+        return GEMM_SRCS
+    own = KERNEL_SRC.get(kname.split()[0])
+    if own is None:
+        raise ValueError("no source known for kernel %r" % kname)
+    return SHARED_SRCS + [os.path.join(_CSRC, own)]
+
+
+def source_hash(kname=None):
+    """First 16 hex digits of sha256 over the kernel sources (comments
+    removed; those of one routed kernel, or of all) and the flags they are
+    compiled with."""
     from bit_prefill_gemm_amd.build import KERNEL_FLAGS
     h = hashlib.sha256()
-    for f in GEMM_SRCS:
+    for f in sorted(set(kernel_srcs(kname))):
         h.update(strip_comments(open(f, encoding="utf-8").read()).encode("utf-8"))
     h.update(" ".join(KERNEL_FLAGS).encode("utf-8"))
     return h.hexdigest()[:16]
@@ -170,16 +219,15 @@ def cpu_model():
     return "unknown"
 
 
-def measured_traffic(workload, bits, out="f32"):
-    """HBM bytes per GEMM launch from the committed counter summary, if still current."""
+def measured_traffic(workload, bits, kname, out="f32"):
+    """HBM bytes per GEMM launch from the committed counter summary, if taken
+    on the same kernel (its name and the hash of its sources are unchanged)."""
     try:
         rec = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
         return None
-    if rec.get("gemm_source_sha256_16") != source_hash():
-        return None
     e = rec.get("workloads", {}).get("%s/%d%s" % (workload, bits, "" if out == "f32" else "/" + out))
-    if not e:
+    if not e or e.get("kernel") != kname or e.get("source_sha256_16") != source_hash(kname):
         return None
     return e["fetch_bytes"] + e["write_bytes"]
 
@@ -252,7 +300,7 @@ def load_data(name, cache):
     return cache[name]
 
 
-def run_gemm(workload, bits, out_kind, steps, warmup, cold_bytes, cache, event_every=EVENT_EVERY):
+def run_gemm(workload, bits, out_kind, steps, warmup, cold_bytes, cache):
     """quantize_act_h32 + w4a4_gemm (or the grouped product) on one workload:
     `steps` timed steps after `warmup`, cycling cold copies of the inputs."""
     import torch
@@ -297,45 +345,30 @@ def run_gemm(workload, bits, out_kind, steps, warmup, cold_bytes, cache, event_e
             f = bb.w4a4_grouped_gemm_bf16 if bf16_out else bb.w4a4_grouped_gemm
             f(codes, scales, bits, offsets, Ws[j], y=y, stream=stream)
 
-    # The GEMM's duration is taken with two events around it on every
-    # event_every-th timed step: each recorded event is one more packet on the
-    # queue and costs the step several microseconds, so recording them on
-    # every step would inflate the step time.  The quantizer's own duration
-    # is taken after the timed region, with events around it alone.
+    # The steps run eagerly, one quantize and one product each, between two
+    # host clock reads around the synchronized stream.  Each kernel's own
+    # duration is taken afterwards from a graph replay of back-to-back launches
+    # over the same cold copies (graph_time_us).
     with torch.cuda.stream(stream):
         for i in range(warmup):
             quantize(i % copies)
             gemm(i % copies)
         torch.cuda.synchronize()
-        evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(2))
-               for _ in range(0, steps, event_every)]
         t0 = time.perf_counter()
         for i in range(steps):
             j = (warmup + i) % copies
             quantize(j)
-            if i % event_every == 0:
-                evs[i // event_every][0].record(stream)
-                gemm(j)
-                evs[i // event_every][1].record(stream)
-            else:
-                gemm(j)
+            gemm(j)
         torch.cuda.synchronize()
         t1 = time.perf_counter()
-        qevs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(2))
-                for _ in range(min(steps, 50))]
-        for i, (e0, e1) in enumerate(qevs):
-            e0.record(stream)
-            quantize(i % copies)
-            e1.record(stream)
-        torch.cuda.synchronize()
+    gemm_ms = graph_time_us(torch, stream, lambda i: gemm(i % copies)) * 1e-3
+    quant_ms = graph_time_us(torch, stream, lambda i: quantize(i % copies)) * 1e-3
 
     ms_per_step = (t1 - t0) * 1e3 / steps
-    quant_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in qevs]))
-    gemm_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
     gemm_s = gemm_ms * 1e-3
     eff_tops = 2.0 * m * n * k / gemm_s / 1e12
     gbytes = gemm_bytes(m, k, n, bits, experts, out_bytes)
-    traffic = measured_traffic(workload, bits, out_kind)
+    traffic = measured_traffic(workload, bits, kname, out_kind)
     entry = ("w4a4_gemm" if experts == 1 else "w4a4_grouped_gemm") + ("_bf16" if bf16_out else "")
     res = {
         "value": wl.get("tokens", m) / (ms_per_step * 1e-3),
@@ -429,8 +462,7 @@ def main():
             if WORKLOADS[name].get("layer"):
                 r, _ = run_layer(bits, args.config_steps, 5, args.cold_bytes, cache)
             else:
-                r, _ = run_gemm(name, bits, "f32", args.config_steps, 5, args.cold_bytes, cache,
-                                event_every=4)
+                r, _ = run_gemm(name, bits, "f32", args.config_steps, 5, args.cold_bytes, cache)
             configs["%s/%d" % (name, bits)] = summary(r)
         out["configs"] = configs
     if not args.no_cpu_baseline:
@@ -506,43 +538,26 @@ def run_layer(bits, steps, warmup, cold_bytes, cache):
 
     gate_name = "w4a4_grouped_gemm_gather"
 
-    def step(j, ev=None):
-        for name, f in kernels.items():
-            if ev is not None and name == gate_name:
-                ev[0].record(stream)
-                f(j)
-                ev[1].record(stream)
-            else:
-                f(j)
+    def step(j):
+        for f in kernels.values():
+            f(j)
 
     with torch.cuda.stream(stream):
         for i in range(warmup):
             step(i % copies)
         torch.cuda.synchronize()
-        gate_evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(2))
-                    for _ in range(0, steps, EVENT_EVERY)]
         t0 = time.perf_counter()
         for i in range(steps):
-            step((warmup + i) % copies,
-                 gate_evs[i // EVENT_EVERY] if i % EVENT_EVERY == 0 else None)
+            step((warmup + i) % copies)
         torch.cuda.synchronize()
         t1 = time.perf_counter()
-        # each kernel's own duration: event pairs around it alone, in step order
-        reps = min(steps, 30)
-        evs = {name: [] for name in kernels}
-        for i in range(reps):
-            j = i % copies
-            for name, f in kernels.items():
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
-                f(j)
-                e1.record(stream)
-                evs[name].append((e0, e1))
-        torch.cuda.synchronize()
-    kernel_us = {name: 1e3 * float(np.mean([a.elapsed_time(b) for a, b in v]))
-                 for name, v in evs.items()}
+    # each kernel's own duration: a graph replay of back-to-back launches of
+    # it alone over the cold copies (every kernel of the step rewrites its
+    # outputs from its inputs, so repeating one is the same work each time)
+    kernel_us = {name: graph_time_us(torch, stream, lambda i, f=f: f(i % copies))
+                 for name, f in kernels.items()}
     ms_per_step = (t1 - t0) * 1e3 / steps
-    gate_s = float(np.mean([a.elapsed_time(b) for a, b in gate_evs])) * 1e-3
+    gate_s = kernel_us[gate_name] * 1e-6
     kname = bb.w4a4_grouped_gemm_kernel_name(bits, rows, Wgu0, src_rows=T)
     roofline = roofline_of("w4a4_grouped_gemm_gather: " + kname, rows, H, 2 * I, bits, E, gate_s,
                            None)

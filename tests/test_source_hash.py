@@ -29,6 +29,19 @@ def test_hash_is_stable_and_covers_the_kernels():
             "internal.h"} <= names
 
 
+def test_kernel_hash_covers_its_own_source_only():
+    """The hash keyed to one routed kernel covers its own file and the shared
+    routing and operand code, not the other kernels' files."""
+    srcs = {os.path.basename(f) for f in bench.kernel_srcs("weight-stream")}
+    assert srcs == {"gemm.hip", "operands.h", "internal.h", "skinny.hip"}
+    assert {os.path.basename(f) for f in bench.kernel_srcs("wide 64x160")} >= {"wide.hip"}
+    assert "wide.hip" not in {os.path.basename(f) for f in bench.kernel_srcs("strip 32x128")}
+    for name in ("tiled 64x160", "expert-slot", "grouped 32x128", "strip 32x128"):
+        h = bench.source_hash(name)
+        assert len(h) == 16 and h == bench.source_hash(name)
+    assert bench.source_hash("wide 64x160") != bench.source_hash("strip 32x128")
+
+
 def test_hash_covers_the_compile_flags(monkeypatch):
     """A change of the code-generation flags changes the hash (so counters
     taken with other flags are not reported as current); include paths,
