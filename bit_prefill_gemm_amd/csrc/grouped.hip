@@ -360,14 +360,19 @@ __global__ __launch_bounds__(256, 2) void grouped_kernel(GemmProblem p, int tile
         Acc Dp;
         float dwp = 0.0f, nbp = 0.0f;
         float4 dap[4];
+        // the activation operand of block q is read one block ahead, so its
+        // LDS latency overlaps block q-1's matrix instruction and epilogue
+        uint2 adn = *reinterpret_cast<const uint2 *>(buf + (ah + a_rd + (uint32_t)(csw * 16)));
 #pragma unroll
         for (int q = 0; q <= C::kSB; q++) {
             Acc Dc;
             float dwc = 0.0f, nbc = 0.0f;
             float4 dac[4];
             if (q < C::kSB) {
-                const uint2 ad = *reinterpret_cast<const uint2 *>(
-                    buf + (ah + a_rd + (uint32_t)((q ^ csw) * 16)));
+                const uint2 ad = adn;
+                if (q + 1 < C::kSB)
+                    adn = *reinterpret_cast<const uint2 *>(
+                        buf + (ah + a_rd + (uint32_t)(((q + 1) ^ csw) * 16)));
                 Op a;
                 a[0] = (int)act_lo(ad.x);
                 a[1] = (int)act_lo(ad.y);
