@@ -17,12 +17,18 @@ tokens), and the whole expert layer (moe512_layer: expert sort, token
 quantization, gathered gate/up GEMM, SwiGLU-rotate-quantize, down GEMM,
 weighted combine; `kernel_us` gives each kernel's own duration).
 
-Prints ONE JSON line.  `value` is prompt tokens per second of the step.  The
+Prints ONE JSON line.  `value` is prompt tokens per second of the step: the
+K timed steps are one captured graph replayed between two synchronisations
+(after W untimed steps), and `eager_step_us` gives the same steps issued one
+binding call at a time.  The
 `roofline` object covers the GEMM kernel (the dominant kernel).  Its average
 duration is measured with HIP events recorded on the launch stream around a
 graph replay of 40 back-to-back GEMM launches over the same cold copies,
 right after the timed steps (an event pair around each single launch would
-add its two queue packets to every launch).  The bound is whichever algorithmic floor
+add its two queue packets to every launch).  `gemm_in_step_us` is the same
+kernel inside whole steps: a graph replay of quantize + GEMM steps less the
+quantizer's own replay (the product right after the quantizer that wrote its
+codes runs a few percent longer than back to back).  The bound is whichever algorithmic floor
 of the contraction is larger: its 2*M*N*K integer ops at the dense int8
 matrix peak ("mfma"), or its HBM bytes at the HBM peak ("hbm": a few rows, and
 the grouped expert GEMMs, whose weight stream is larger).  `epilogue_valu`
@@ -105,6 +111,47 @@ CONFIG_RUNS = [("attn512", 8), ("ffn512_gate", 4), ("ffn512_down", 4), ("ffn512_
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_traffic.json")
 GRAPH_LAUNCHES = 40   # launches per captured graph when a kernel is timed alone
 GRAPH_REPLAYS = 5
+
+
+def timed_steps(torch, stream, step, steps, warmup, copies):
+    """(ms per step, ms per eager step).  The timed region replays one
+    captured graph of `steps` steps, step j = (warmup + i) % copies, between
+    two synchronisations of the device, after an untimed replay of `warmup`
+    steps.  Replaying a captured sequence is how a fixed prompt pipeline runs
+    on the device (no host work between the kernels); the same steps issued
+    one binding call at a time are timed as well, for comparison (larger
+    shapes lose 4-19% that way, the 16-row ones are bound by the binding's
+    host time)."""
+    with torch.cuda.stream(stream):
+        for i in range(warmup):
+            step(i % copies)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            step((warmup + i) % copies)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+    eager_ms = (t1 - t0) * 1e3 / steps
+    graphs = []
+    for n, first in ((warmup, 0), (steps, warmup)):
+        g = None
+        if n > 0:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                for i in range(n):
+                    step((first + i) % copies)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        if graphs[0] is not None:
+            graphs[0].replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        graphs[1].replay()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+    del graphs
+    return (t1 - t0) * 1e3 / steps, eager_ms
 
 
 def graph_time_us(torch, stream, launch, n=GRAPH_LAUNCHES, replays=GRAPH_REPLAYS):
@@ -345,26 +392,22 @@ def run_gemm(workload, bits, out_kind, steps, warmup, cold_bytes, cache):
             f = bb.w4a4_grouped_gemm_bf16 if bf16_out else bb.w4a4_grouped_gemm
             f(codes, scales, bits, offsets, Ws[j], y=y, stream=stream)
 
-    # The steps run eagerly, one quantize and one product each, between two
-    # host clock reads around the synchronized stream.  Each kernel's own
-    # duration is taken afterwards from a graph replay of back-to-back launches
-    # over the same cold copies (graph_time_us).
-    with torch.cuda.stream(stream):
-        for i in range(warmup):
-            quantize(i % copies)
-            gemm(i % copies)
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for i in range(steps):
-            j = (warmup + i) % copies
-            quantize(j)
-            gemm(j)
-        torch.cuda.synchronize()
-        t1 = time.perf_counter()
+    def step(j):
+        quantize(j)
+        gemm(j)
+
+    # The timed steps (one quantize and one product each) replay one captured
+    # graph; the same steps issued eagerly are timed too (eager_step_us).
+    # Each kernel's own duration is taken afterwards from a graph replay of
+    # back-to-back launches over the same cold copies (graph_time_us).
+    ms_per_step, eager_ms = timed_steps(torch, stream, step, steps, warmup, copies)
     gemm_ms = graph_time_us(torch, stream, lambda i: gemm(i % copies)) * 1e-3
     quant_ms = graph_time_us(torch, stream, lambda i: quantize(i % copies)) * 1e-3
+    # whole steps replayed the same way: the product right after the quantizer
+    # that wrote its codes runs a few percent longer than back to back
+    step_graph_ms = graph_time_us(torch, stream,
+                                  lambda i: (quantize(i % copies), gemm(i % copies))) * 1e-3
 
-    ms_per_step = (t1 - t0) * 1e3 / steps
     gemm_s = gemm_ms * 1e-3
     eff_tops = 2.0 * m * n * k / gemm_s / 1e12
     gbytes = gemm_bytes(m, k, n, bits, experts, out_bytes)
@@ -387,7 +430,10 @@ def run_gemm(workload, bits, out_kind, steps, warmup, cold_bytes, cache):
         "pct_int8_peak": 100.0 * eff_tops / (PEAK_INT8_OPS / 1e12),
         "gemm_us": gemm_ms * 1e3,
         "quant_us": quant_ms * 1e3,
+        "step_graph_us": step_graph_ms * 1e3,
+        "gemm_in_step_us": (step_graph_ms - quant_ms) * 1e3,
         "step_us": ms_per_step * 1e3,
+        "eager_step_us": eager_ms * 1e3,
         "gemm_hbm_GBps": gbytes / gemm_s / 1e9,
         "pct_hbm": 100.0 * gbytes / gemm_s / PEAK_HBM,
         "gemm_algorithmic_bytes": gbytes,
@@ -401,11 +447,14 @@ def run_gemm(workload, bits, out_kind, steps, warmup, cold_bytes, cache):
 def summary(res):
     """The per-workload entry of `configs`."""
     if "kernel_us" in res:
-        return {"step_us": res["step_us"], "tokens_per_s": res["value"],
+        return {"step_us": res["step_us"], "eager_step_us": res["eager_step_us"],
+                "tokens_per_s": res["value"],
                 "kernel_us": res["kernel_us"], "roofline": res["roofline"]}
     r = res["roofline"]
     return {"kernel": res["kernel"], "gemm_us": res["gemm_us"], "quant_us": res["quant_us"],
-            "step_us": res["step_us"], "tokens_per_s": res["value"],
+            "gemm_in_step_us": res["gemm_in_step_us"],
+            "step_us": res["step_us"], "eager_step_us": res["eager_step_us"],
+            "tokens_per_s": res["value"],
             "roofline": {"bound": r["bound"], "frac": r["frac"], "achieved": r["achieved"],
                          "unit": r["unit"], "traffic": r["traffic"]},
             "int8_frac": res["pct_int8_peak"] / 100.0, "hbm_frac": res["pct_hbm"] / 100.0,
@@ -542,21 +591,12 @@ def run_layer(bits, steps, warmup, cold_bytes, cache):
         for f in kernels.values():
             f(j)
 
-    with torch.cuda.stream(stream):
-        for i in range(warmup):
-            step(i % copies)
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for i in range(steps):
-            step((warmup + i) % copies)
-        torch.cuda.synchronize()
-        t1 = time.perf_counter()
+    ms_per_step, eager_ms = timed_steps(torch, stream, step, steps, warmup, copies)
     # each kernel's own duration: a graph replay of back-to-back launches of
     # it alone over the cold copies (every kernel of the step rewrites its
     # outputs from its inputs, so repeating one is the same work each time)
     kernel_us = {name: graph_time_us(torch, stream, lambda i, f=f: f(i % copies))
                  for name, f in kernels.items()}
-    ms_per_step = (t1 - t0) * 1e3 / steps
     gate_s = kernel_us[gate_name] * 1e-6
     kname = bb.w4a4_grouped_gemm_kernel_name(bits, rows, Wgu0, src_rows=T)
     roofline = roofline_of("w4a4_grouped_gemm_gather: " + kname, rows, H, 2 * I, bits, E, gate_s,
@@ -572,6 +612,7 @@ def run_layer(bits, steps, warmup, cold_bytes, cache):
         "roofline": roofline,
         "kernel_us": kernel_us,
         "step_us": ms_per_step * 1e3,
+        "eager_step_us": eager_ms * 1e3,
         "routes": (e_np, w_np),
     }
     del Wgu, Wdn, xs, gu_img, dn_img, x0
