@@ -18,7 +18,8 @@
 //     barriers in the main loop), with D groups of loads in flight per wave
 //     while a group is computed;
 //   - the few activation rows are staged once per workgroup in LDS when they
-//     fit (16 rows of K <= 6144 4-bit codes): read with whole cache lines and
+//     and the transposed row scales fit 64 KB (16 rows, K <= 6528 with 4-bit
+//     codes, K <= 3616 with 8-bit ones): read with whole cache lines and
 //     stored with a padded row stride, so a wave's operand read of 16 rows
 //     hits 16 distinct bank groups.  Read from L2 with every group instead,
 //     each 16-lane quarter of an activation load touches 16 rows, i.e. 16

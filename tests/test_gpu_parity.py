@@ -210,6 +210,18 @@ def test_gemm_few_rows_long_k(torch, k):
     check_gemm(case["x"], case["w"], 64, k, 4, label="few rows long K")
 
 
+@pytest.mark.parametrize("bits,k", [(4, 6528), (4, 6560), (8, 3616), (8, 3648)])
+@pytest.mark.parametrize("m", [5, 16])
+def test_gemm_few_rows_staged_limit(torch, m, k, bits):
+    """The weight-stream kernel stages its activation rows in LDS while they
+    and the transposed row scales fit 64 KB: the largest such K for each code
+    width, and one block more (rows read from L2 with every group)."""
+    case = synth.small_dense(m, k, 64, seed=m + k + bits)
+    W = weights_to_device(case["w"], 64, k)
+    assert bb.w4a4_gemm_kernel_name(bits, m, W) == "weight-stream"
+    check_gemm(case["x"], case["w"], 64, k, bits, label="few rows staged limit")
+
+
 def test_gemm_few_rows_output_stride(torch):
     case = synth.small_dense(20, 160, 96, seed=5)
     codes, scales, q, d = quantize_and_check(case["x"], 8)
