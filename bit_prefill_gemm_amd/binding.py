@@ -130,15 +130,23 @@ def _torch():
     return torch
 
 
-def _stream_handle(stream):
+def _stream_handle(stream, device=None):
+    """The hipStream_t of `stream`, or of the current stream of `device` (an
+    int, e.g. a tensor's get_device(); the current device if None) as an int.
+    The raw query of torch's current stream costs a tenth of building the
+    stream object; torch builds without it fall back to that."""
+    if stream is not None:
+        return stream.cuda_stream
     torch = _torch()
-    if stream is None:
-        stream = torch.cuda.current_stream()
-    return ctypes.c_void_p(stream.cuda_stream)
+    raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+    if raw is not None:
+        return raw(device if device is not None and device >= 0 else torch.cuda.current_device())
+    return torch.cuda.current_stream().cuda_stream
 
 
 def _dptr(t):
-    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+    """A tensor's device address as an int (ctypes passes it as void *), 0 for None."""
+    return t.data_ptr() if t is not None else 0
 
 
 # Argument checks.  The C ABI sees only pointers and sizes, so a tensor of the
@@ -159,7 +167,7 @@ def _tensor(where, name, t, dtypes, shape, contiguous=True):
     if t.dtype not in dtypes:
         _fail(where, "%s has dtype %s, expected %s" % (name, t.dtype,
                                                        " or ".join(str(d) for d in dtypes)))
-    if tuple(t.shape) != tuple(shape):
+    if t.shape != tuple(shape):
         _fail(where, "%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
     if contiguous and not t.is_contiguous():
         _fail(where, "%s must be contiguous" % name)
@@ -173,14 +181,17 @@ def _rows_out(where, name, t, dtype, rows, cols):
 
 
 def _same_device(where, *tensors):
-    """Every tensor on one cuda device (checked last: see above)."""
-    devs = {t.device for t in tensors if t is not None}
-    if any(d.type != "cuda" for d in devs):
-        _fail(where, "every tensor must be on a cuda device (got %s)"
-              % ", ".join(sorted(str(d) for d in devs)))
-    if len(devs) > 1:
+    """Every tensor on one cuda device (checked last: see above); returns its
+    index.  get_device() is -1 for a host tensor."""
+    idx = {t.get_device() for t in tensors if t is not None}
+    if -1 in idx or len(idx) > 1:
+        devs = {t.device for t in tensors if t is not None}
+        if any(d.type != "cuda" for d in devs):
+            _fail(where, "every tensor must be on a cuda device (got %s)"
+                  % ", ".join(sorted(str(d) for d in devs)))
         _fail(where, "tensors are on different devices: %s"
               % ", ".join(sorted(str(d) for d in devs)))
+    return idx.pop() if idx else None
 
 
 def _check_bits(where, act_bits):
@@ -295,7 +306,7 @@ def _quantize_args(name, x, act_bits, codes, scales, span=32):
 def _quantize(name: str, x, act_bits, codes, scales, stream):
     dt, m, k, codes, scales = _quantize_args(name, x, act_bits, codes, scales)
     st = getattr(_lib_handle(), name)(_dptr(x), dt, m, k, x.stride(0), act_bits, _dptr(codes),
-                                      _dptr(scales), _stream_handle(stream))
+                                      _dptr(scales), _stream_handle(stream, x.get_device()))
     _check(st, name)
     return codes, scales
 
@@ -329,7 +340,7 @@ def _gemm(name: str, codes, scales, act_bits, w, y, stream, dtype=None):
     m, y = _gemm_args(name, codes, scales, act_bits, w, y, dtype or _torch().float32)
     st = getattr(_lib_handle(), name)(_dptr(codes), _dptr(scales), act_bits, m,
                                       ctypes.byref(w.desc), _dptr(w.image), _dptr(y),
-                                      y.stride(0), _stream_handle(stream))
+                                      y.stride(0), _stream_handle(stream, codes.get_device()))
     _check(st, name)
     return y
 
@@ -368,7 +379,7 @@ def _grouped(name, codes, scales, act_bits, expert_offsets, w, y, stream, dtype)
     st = getattr(_lib_handle(), name)(_dptr(codes), _dptr(scales), act_bits, rows,
                                       _dptr(expert_offsets), ctypes.byref(w.desc),
                                       _dptr(w.image), _dptr(y), y.stride(0),
-                                      _stream_handle(stream))
+                                      _stream_handle(stream, codes.get_device()))
     _check(st, name)
     return y
 
@@ -407,7 +418,8 @@ def w4a4_gemm_blocksums(codes, scales, act_bits: int, w: Weights, m0: int, m1: i
     _same_device(where, codes, w.image, sums, scales if isinstance(scales, torch.Tensor) else None)
     st = _lib_handle().w4a4_gemm_blocksums(_dptr(codes), _dptr(scales), act_bits, m,
                                            ctypes.byref(w.desc), _dptr(w.image), expert, m0, m1,
-                                           n0, n1, _dptr(sums), _stream_handle(stream))
+                                           n0, n1, _dptr(sums),
+                                                         _stream_handle(stream, codes.get_device()))
     _check(st, "w4a4_gemm_blocksums")
     return sums
 
@@ -443,7 +455,8 @@ def moe_route_sort(expert_of, tokens: int, topk: int, experts: int, stream=None)
     row_token = torch.empty(n, dtype=torch.int32, device=dev)
     slot_of = torch.empty(n, dtype=torch.int32, device=dev)
     st = _lib_handle().moe_route_sort(_dptr(expert_of), tokens, topk, experts, _dptr(offsets),
-                                      _dptr(row_token), _dptr(slot_of), _stream_handle(stream))
+                                      _dptr(row_token), _dptr(slot_of),
+                                      _stream_handle(stream, expert_of.get_device()))
     _check(st, "moe_route_sort")
     return offsets, row_token, slot_of
 
@@ -469,7 +482,8 @@ def w4a4_grouped_gemm_gather(codes, scales, act_bits: int, row_ids, expert_offse
     st = _lib_handle().w4a4_grouped_gemm_gather(_dptr(codes), _dptr(scales), act_bits, src_rows,
                                                 _dptr(row_ids), rows, _dptr(expert_offsets),
                                                 ctypes.byref(w.desc), _dptr(w.image), _dptr(y),
-                                                y.stride(0), _stream_handle(stream))
+                                                y.stride(0),
+                                                         _stream_handle(stream, codes.get_device()))
     _check(st, "w4a4_grouped_gemm_gather")
     return y
 
@@ -494,7 +508,8 @@ def swiglu_quantize_h32(gu, inter: int, act_bits: int = 4, codes=None, scales=No
     _check_codes(where, codes, scales, act_bits, rows, inter)
     _same_device(where, gu, codes, scales)
     st = _lib_handle().swiglu_quantize_h32(_dptr(gu), rows, inter, gu.stride(0), act_bits,
-                                           _dptr(codes), _dptr(scales), _stream_handle(stream))
+                                           _dptr(codes), _dptr(scales),
+                                           _stream_handle(stream, gu.get_device()))
     _check(st, "swiglu_quantize_h32")
     return codes, scales
 
@@ -515,7 +530,7 @@ def moe_combine(dn, slot_of, weights, tokens: int, topk: int, y=None, stream=Non
     _same_device(where, dn, slot_of, weights, y)
     st = _lib_handle().moe_combine(_dptr(dn), dn.stride(0), rows, _dptr(slot_of), _dptr(weights),
                                    tokens, topk, hidden, _dptr(y), y.stride(0),
-                                   _stream_handle(stream))
+                                   _stream_handle(stream, dn.get_device()))
     _check(st, "moe_combine")
     return y
 
@@ -543,7 +558,8 @@ def quantize_act_rot(x, rotation: int, act_bits: int = 4, codes=None, scales=Non
     dt, m, k, codes, scales = _quantize_args("quantize_act_rot", x, act_bits, codes, scales,
                                              span=rotation)
     st = _lib_handle().quantize_act_rot(_dptr(x), dt, m, k, x.stride(0), act_bits, rotation,
-                                        _dptr(codes), _dptr(scales), _stream_handle(stream))
+                                        _dptr(codes), _dptr(scales),
+                                                            _stream_handle(stream, x.get_device()))
     _check(st, "quantize_act_rot")
     return codes, scales
 
@@ -552,6 +568,6 @@ def w4a4_gemm_rot(codes, scales, act_bits: int, rotation: int, w: Weights, y=Non
     m, y = _gemm_args("w4a4_gemm_rot", codes, scales, act_bits, w, y, _torch().float32)
     st = _lib_handle().w4a4_gemm_rot(_dptr(codes), _dptr(scales), act_bits, rotation, m,
                                      ctypes.byref(w.desc), _dptr(w.image), _dptr(y), y.stride(0),
-                                     _stream_handle(stream))
+                                     _stream_handle(stream, codes.get_device()))
     _check(st, "w4a4_gemm_rot")
     return y
