@@ -18,9 +18,11 @@ quantization, gathered gate/up GEMM, SwiGLU-rotate-quantize, down GEMM,
 weighted combine; `kernel_us` gives each kernel's own duration).
 
 Prints ONE JSON line.  `value` is prompt tokens per second of the step: the
-K timed steps are one captured graph replayed between two synchronisations
-(after W untimed steps), and `eager_step_us` gives the same steps issued one
-binding call at a time.  The
+K timed steps are one captured graph, uploaded to the device beforehand and
+replayed between two synchronisations right after an untimed replay of the W
+warm-up steps (an idle GPU's clock needs tens of milliseconds of load to come
+up; the default W covers that), and `eager_step_us` gives the same steps
+issued one binding call at a time.  The
 `roofline` object covers the GEMM kernel (the dominant kernel).  Its average
 duration is measured with HIP events recorded on the launch stream around a
 graph replay of 40 back-to-back GEMM launches over the same cold copies,
@@ -51,6 +53,7 @@ infrastructure, not the product path).
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import math
@@ -113,25 +116,37 @@ GRAPH_LAUNCHES = 40   # launches per captured graph when a kernel is timed alone
 GRAPH_REPLAYS = 5
 
 
+def upload_graph(torch, graph, stream):
+    """Upload a captured graph's executable to the device before it first
+    runs (hipGraphUpload), so that its first replay does not pay for it.
+    Skipped where the runtime or this PyTorch does not offer it."""
+    exec_handle = getattr(graph, "raw_cuda_graph_exec", None)
+    if exec_handle is None:
+        return
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+        fn = hip.hipGraphUpload
+    except (OSError, AttributeError):
+        return
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    fn.restype = ctypes.c_int
+    rc = fn(ctypes.c_void_p(exec_handle()), ctypes.c_void_p(stream.cuda_stream))
+    if rc != 0:
+        raise RuntimeError("hipGraphUpload failed (%d)" % rc)
+
+
 def timed_steps(torch, stream, step, steps, warmup, copies):
-    """(ms per step, ms per eager step).  The timed region replays one
-    captured graph of `steps` steps, step j = (warmup + i) % copies, between
-    two synchronisations of the device, after an untimed replay of `warmup`
-    steps.  Replaying a captured sequence is how a fixed prompt pipeline runs
-    on the device (no host work between the kernels); the same steps issued
-    one binding call at a time are timed as well, for comparison (larger
-    shapes lose 4-19% that way, the 16-row ones are bound by the binding's
-    host time)."""
-    with torch.cuda.stream(stream):
-        for i in range(warmup):
-            step(i % copies)
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for i in range(steps):
-            step((warmup + i) % copies)
-        torch.cuda.synchronize()
-        t1 = time.perf_counter()
-    eager_ms = (t1 - t0) * 1e3 / steps
+    """(ms per step, ms per eager step).  The warm-up steps and the timed
+    steps are captured as two graphs (step j = j % copies, the timed ones
+    following the warm-up ones) and uploaded to the device; the warm-up graph
+    is replayed untimed, then the timed region replays the `steps` steps
+    between two synchronisations of the device.  Replaying a captured sequence
+    is how a fixed prompt pipeline runs on the device (no host work between
+    the kernels).  The clock of an idle GPU takes tens of milliseconds of
+    load to come up, which is what the warm-up steps are for.  The same steps
+    issued one binding call at a time are timed afterwards, for comparison
+    (larger shapes lose a few percent that way, the 16-row ones are bound by
+    the binding's host time)."""
     graphs = []
     for n, first in ((warmup, 0), (steps, warmup)):
         g = None
@@ -142,6 +157,10 @@ def timed_steps(torch, stream, step, steps, warmup, copies):
                     step((first + i) % copies)
         graphs.append(g)
     torch.cuda.synchronize()
+    for g in graphs:
+        if g is not None:
+            upload_graph(torch, g, stream)
+    torch.cuda.synchronize()
     with torch.cuda.stream(stream):
         if graphs[0] is not None:
             graphs[0].replay()
@@ -151,7 +170,17 @@ def timed_steps(torch, stream, step, steps, warmup, copies):
         torch.cuda.synchronize()
         t1 = time.perf_counter()
     del graphs
-    return (t1 - t0) * 1e3 / steps, eager_ms
+    graph_ms = (t1 - t0) * 1e3 / steps
+    with torch.cuda.stream(stream):
+        for i in range(warmup):
+            step(i % copies)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            step((warmup + i) % copies)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+    return graph_ms, (t1 - t0) * 1e3 / steps
 
 
 def graph_time_us(torch, stream, launch, n=GRAPH_LAUNCHES, replays=GRAPH_REPLAYS):
@@ -186,7 +215,7 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=400)
     ap.add_argument("--workload", default="attn512", choices=sorted(WORKLOADS))
     ap.add_argument("--bits", type=int, default=4, choices=(4, 8))
     ap.add_argument("--out", default="f32", choices=("f32", "bf16"),
@@ -197,6 +226,7 @@ def parse():
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the other workloads (measured only with the default one)")
     ap.add_argument("--config-steps", type=int, default=40)
+    ap.add_argument("--config-warmup", type=int, default=200)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration", type=float, default=0.0)
     return ap.parse_args()
@@ -509,9 +539,11 @@ def main():
                 continue
             print("config %s %d-bit" % (name, bits), file=sys.stderr, flush=True)
             if WORKLOADS[name].get("layer"):
-                r, _ = run_layer(bits, args.config_steps, 5, args.cold_bytes, cache)
+                r, _ = run_layer(bits, args.config_steps, args.config_warmup, args.cold_bytes,
+                                 cache)
             else:
-                r, _ = run_gemm(name, bits, "f32", args.config_steps, 5, args.cold_bytes, cache)
+                r, _ = run_gemm(name, bits, "f32", args.config_steps, args.config_warmup,
+                                args.cold_bytes, cache)
             configs["%s/%d" % (name, bits)] = summary(r)
         out["configs"] = configs
     if not args.no_cpu_baseline:
