@@ -19,26 +19,34 @@ namespace {
 
 constexpr int kSortThreads = 256;
 
-// Inclusive scan of one int per thread over the workgroup (kSortThreads),
-// in thread order; `wsum` is LDS of kSortThreads / 64 ints.
-__device__ __forceinline__ int block_scan_incl(int v, int *wsum)
+// Inclusive scans of two ints per thread over the workgroup (kSortThreads),
+// in thread order, with one pair of barriers; `wsum` is LDS of 2 *
+// kSortThreads / 64 ints.
+__device__ __forceinline__ int2 block_scan_incl2(int a, int b, int *wsum)
 {
+    constexpr int kW = kSortThreads / 64;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    int incl = v;
+    int ia = a, ib = b;
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
-        const int u = __shfl_up(incl, d);
-        if (lane >= d)
-            incl += u;
+        const int ua = __shfl_up(ia, d), ub = __shfl_up(ib, d);
+        if (lane >= d) {
+            ia += ua;
+            ib += ub;
+        }
     }
-    if (lane == 63)
-        wsum[wave] = incl;
+    if (lane == 63) {
+        wsum[wave] = ia;
+        wsum[kW + wave] = ib;
+    }
     __syncthreads();
-    int before = 0;
-    for (int w = 0; w < wave; w++)
-        before += wsum[w];
+    int ba = 0, bb = 0;
+    for (int w = 0; w < wave; w++) {
+        ba += wsum[w];
+        bb += wsum[kW + w];
+    }
     __syncthreads();
-    return before + incl;
+    return make_int2(ba + ia, bb + ib);
 }
 
 // Counting sort with one workgroup per expert x.  Thread t owns the
@@ -46,35 +54,62 @@ __device__ __forceinline__ int block_scan_incl(int v, int *wsum)
 // before x and of x itself; the sum of the first counts over the workgroup is
 // x's offset, and a scan of the second over the threads in order gives each
 // entry of x its place: the stable order.  Expert ids outside [0, experts)
-// are clamped (the rows stay in bounds).
+// are clamped (the rows stay in bounds).  Ranges of up to kCached entries
+// read with 16-byte loads stay in registers between the count and the
+// placement; longer ones are read again.
+constexpr int kCached = 16;
+
 __global__ __launch_bounds__(kSortThreads) void route_sort_kernel(
     const int32_t *__restrict__ expert_of, int n, int topk, int experts,
     int32_t *__restrict__ offsets, int32_t *__restrict__ row_token, int32_t *__restrict__ slot_of)
 {
-    __shared__ int wsum[kSortThreads / 64];
-    __shared__ int off_sh;
+    __shared__ int wsum[2 * kSortThreads / 64];
     const int x = blockIdx.x, tid = threadIdx.x;
     const int per = (n + kSortThreads - 1) / kSortThreads;
     const int lo = tid * per < n ? tid * per : n;
     const int hi = lo + per < n ? lo + per : n;
-    auto expert_at = [&](int i) {
-        const int e = expert_of[i];
-        return e < 0 ? 0 : (e >= experts ? experts - 1 : e);
-    };
+    auto clamp_e = [&](int e) { return e < 0 ? 0 : (e >= experts ? experts - 1 : e); };
+    auto expert_at = [&](int i) { return clamp_e(expert_of[i]); };
     // 16-byte loads where the range and the pointer allow them
     const bool vec = per % 4 == 0 && (reinterpret_cast<uintptr_t>(expert_of) & 15) == 0;
+    const bool cached = vec && per <= kCached;
     int before = 0, mine = 0; // entries of experts below x, and of x
     auto count = [&](int e) {
         before += e < x;
         mine += e == x;
     };
-    if (vec) {
+    int ec[kCached]; // the range's experts when cached (entries past hi: -1)
+    if (cached) {
+#pragma unroll
+        for (int u = 0; u < kCached / 4; u++) {
+            const int i0 = lo + 4 * u;
+            int ev[4] = {-1, -1, -1, -1};
+            if (i0 + 4 <= hi) {
+                const int4 v = *reinterpret_cast<const int4 *>(expert_of + i0);
+                ev[0] = clamp_e(v.x);
+                ev[1] = clamp_e(v.y);
+                ev[2] = clamp_e(v.z);
+                ev[3] = clamp_e(v.w);
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; j++)
+                    if (i0 + j < hi)
+                        ev[j] = expert_at(i0 + j);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                ec[4 * u + j] = ev[j];
+                if (ev[j] >= 0)
+                    count(ev[j]);
+            }
+        }
+    } else if (vec) {
         for (int i = lo; i + 4 <= hi; i += 4) {
             const int4 v = *reinterpret_cast<const int4 *>(expert_of + i);
             const int ev[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
             for (int j = 0; j < 4; j++)
-                count(ev[j] < 0 ? 0 : (ev[j] >= experts ? experts - 1 : ev[j]));
+                count(clamp_e(ev[j]));
         }
         for (int i = lo + (hi - lo) / 4 * 4; i < hi; i++)
             count(expert_at(i));
@@ -82,14 +117,13 @@ __global__ __launch_bounds__(kSortThreads) void route_sort_kernel(
         for (int i = lo; i < hi; i++)
             count(expert_at(i));
     }
-    // offset of x: the entries of the experts before it
-    const int offset = block_scan_incl(before, wsum);
-    if (tid == kSortThreads - 1)
-        off_sh = offset;
-    __syncthreads();
-    const int base_x = off_sh;
-    // places of this thread's entries of expert x
-    const int incl = block_scan_incl(mine, wsum);
+    // x's offset (the entries of the experts before it) and the places of
+    // this thread's entries of x
+    const int2 incl = block_scan_incl2(before, mine, wsum);
+    int base_x = 0;
+#pragma unroll
+    for (int w = 0; w < kSortThreads / 64; w++)
+        base_x += wsum[w];
     if (tid == 0) {
         offsets[x] = base_x;
         if (x == experts - 1)
@@ -97,7 +131,17 @@ __global__ __launch_bounds__(kSortThreads) void route_sort_kernel(
     }
     if (mine == 0)
         return;
-    int pos = base_x + incl - mine;
+    int pos = base_x + incl.y - mine;
+    if (cached) {
+#pragma unroll
+        for (int j = 0; j < kCached; j++)
+            if (ec[j] == x) {
+                slot_of[lo + j] = pos;
+                row_token[pos] = (lo + j) / topk;
+                pos++;
+            }
+        return;
+    }
     for (int i = lo; i < hi; i++)
         if (expert_at(i) == x) {
             slot_of[i] = pos;

@@ -42,8 +42,11 @@ def sort_and_check(expert_of, tokens, topk, experts):
     return off, row_token, slot_of
 
 
+# entries per thread (of 256): 16 with 16-byte loads kept in registers (512 x 8;
+# 1000 x 4 with a partial last range), 32 with 16-byte loads read twice
+# (1024 x 8), 10 and 1 with 4-byte loads (300 x 8, the small ones)
 @pytest.mark.parametrize("tokens,topk,experts", [(512, 8, 128), (1, 1, 1), (3, 2, 5),
-                                                 (1000, 4, 64), (300, 8, 512)])
+                                                 (1000, 4, 64), (300, 8, 512), (1024, 8, 128)])
 def test_route_sort(torch, tokens, topk, experts):
     rng = np.random.default_rng(tokens + topk + experts)
     e, _ = synth.draw_routes(rng, tokens, experts, topk)
