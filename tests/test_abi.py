@@ -125,6 +125,16 @@ def test_zero_rows_accept_null_buffers():
     assert gemm(codes=NUL, m=1) == NULL
 
 
+def test_gemm_k_limit():
+    """K up to 2^22 passes every host check (then the device check, without a
+    GPU); one block more is refused before any HIP call."""
+    if os.path.exists("/dev/kfd"):
+        pytest.skip("host has a GPU driver")
+    assert gemm(desc=good_desc(k=1 << 22)) == DEVICE
+    assert gemm(desc=good_desc(k=(1 << 22) + 32)) == SHAPE
+    assert sums(desc=good_desc(k=(1 << 22) + 32)) == SHAPE
+
+
 def test_gemm_null_desc():
     lib = bb.lib()
     assert lib.w4a4_gemm(P, P2, 4, 4, None, P, P2, 64, NUL) == NULL

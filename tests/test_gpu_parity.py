@@ -210,6 +210,20 @@ def test_gemm_few_rows_long_k(torch, k):
     check_gemm(case["x"], case["w"], 64, k, 4, label="few rows long K")
 
 
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("m,k,n,kernel", [(5, 1 << 22, 32, "tiled 16x32"),
+                                          (33, 1 << 20, 128, "strip 32x128")])
+def test_gemm_max_k(torch, m, k, n, kernel, bits):
+    """K at the boundary's limit, 2^22 values (131072 blocks: the largest K whose
+    per-workgroup operand offsets stay 32-bit), on the kernel few rows route
+    to there, and 2^20 on the strip kernel; the oracle on sampled rows."""
+    case = synth.small_dense(m, k, n, seed=m + bits)
+    W = weights_to_device(case["w"], n, k)
+    assert bb.w4a4_gemm_kernel_name(bits, m, W) == kernel
+    rows = None if m <= 8 else sample_rows(m, 3, seed=m)
+    check_gemm(case["x"], case["w"], n, k, bits, rows=rows, label="max K")
+
+
 @pytest.mark.parametrize("bits,k", [(4, 6528), (4, 6560), (8, 3616), (8, 3648)])
 @pytest.mark.parametrize("m", [5, 16])
 def test_gemm_few_rows_staged_limit(torch, m, k, bits):
