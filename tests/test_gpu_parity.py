@@ -211,15 +211,18 @@ def test_gemm_few_rows_long_k(torch, k):
 
 
 @pytest.mark.parametrize("bits", [4, 8])
-@pytest.mark.parametrize("m,k,n,kernel", [(5, 1 << 22, 32, "tiled 16x32"),
-                                          (33, 1 << 20, 128, "strip 32x128")])
-def test_gemm_max_k(torch, m, k, n, kernel, bits):
+@pytest.mark.parametrize("m,k,n,kernels", [
+    (5, 1 << 22, 32, ("tiled 16x32", "tiled 16x32")),
+    (33, 1 << 20, 128, ("strip 32x128", "strip 32x128")),
+    (512, 1 << 16, 5120, ("wide 64x160", "tiled 64x160"))])
+def test_gemm_max_k(torch, m, k, n, kernels, bits):
     """K at the boundary's limit, 2^22 values (131072 blocks: the largest K whose
     per-workgroup operand offsets stay 32-bit), on the kernel few rows route
-    to there, and 2^20 on the strip kernel; the oracle on sampled rows."""
+    to there; 2^20 on the strip kernel and 2^16 (128 stages of 16 blocks) on
+    the 64 x 160 tiles; the oracle on sampled rows."""
     case = synth.small_dense(m, k, n, seed=m + bits)
     W = weights_to_device(case["w"], n, k)
-    assert bb.w4a4_gemm_kernel_name(bits, m, W) == kernel
+    assert bb.w4a4_gemm_kernel_name(bits, m, W) == kernels[0 if bits == 4 else 1]
     rows = None if m <= 8 else sample_rows(m, 3, seed=m)
     check_gemm(case["x"], case["w"], n, k, bits, rows=rows, label="max K")
 
