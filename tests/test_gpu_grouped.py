@@ -1,7 +1,8 @@
 """GPU parity of the grouped product on 64-row expert slots (the kernel that
 runs 4-bit grouped products with N a multiple of 128 and at most 1024
 experts): slot shapes (empty experts, one row, 32, 33, 64, 65 and several
-slots per expert), K with a partial last stage and with a single stage, many
+slots per expert), K with a partial last stage, with a single stage and long
+(2^18), many
 experts (the slot lookup over several chunks of the table), fewer work items
 than compute units, gathered rows with repeats, repeat runs, and offsets that
 break the ordering rule (accesses stay in bounds; rows that exactly one
@@ -98,6 +99,12 @@ def test_many_experts_lookup(torch):
     rng = np.random.default_rng(53)
     counts = rng.integers(0, 4, size=1000)
     run_grouped(counts, 128, 64, seed=53, rows_extra=80)
+
+
+def test_long_k(torch):
+    # K = 2^18 (8192 blocks, 1024 stages of two groups per item): the weight
+    # image offsets of an expert and the rows' code offsets far from zero
+    run_grouped([33, 0, 70], 128, 1 << 18, seed=56, rows_extra=8)
 
 
 def test_fewer_items_than_compute_units(torch):
