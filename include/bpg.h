@@ -22,8 +22,8 @@
  *   - rotation: Sylvester-order H32, butterfly stages h = 1,2,4,8,16 in fp32
  *     (lower index a+b, upper a-b), then times fp32(1/sqrt(32)); no FMA;
  *   - scale d = amax/7 (8-bit: amax/127), IEEE fp32 division; code
- *     q = clamp(rint(v/d), -8, 7) (8-bit: +-127), ties to even; all-zero block:
- *     d = 0, codes 0;
+ *     q = clamp(rint(v/d), -8, 7) (8-bit: +-127), ties to even; a block with
+ *     d = 0 (all zero, or amax/7 underflowing to 0) has codes 0;
  *   - block dot products are exact int32; the output is
  *     y[m][n] = sum_b da[m][b] * dw[n][b] * S[m][n][b], accumulated in fp32
  *     in a fixed order per shape (bit-identical from run to run).

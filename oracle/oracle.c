@@ -23,8 +23,9 @@
  *     a+b and upper gets a-b, each a single fp32 rounding, then every value is
  *     multiplied by fp32(1/sqrt(32)) (reading: the pages only say "orthogonal");
  *   - scale d = amax/7 (IEEE fp32 division), code q = clamp(rint(v/d), -8, 7)
- *     with round-half-to-even; an all-zero block has d = 0 and codes 0
- *     (reading: the pages give no formula).  The 8-bit route uses amax/127 and
+ *     with round-half-to-even; a block whose scale is 0 (all-zero, or so small
+ *     that amax/7 underflows) has codes 0, which is what every code of it
+ *     dequantizes to (reading: the pages give no formula).  The 8-bit route uses amax/127 and
  *     clamps to +-127 (reading: "exact 8-bit activations" is named, not given);
  *   - a Q4_0 weight code u means u-8 [H32 "Why prompts are a matrix-unit
  *     problem"]; a Q4_0 block is an fp16 scale followed by 16 bytes, byte j
@@ -187,14 +188,13 @@ static int quantize_block(const float v[QK], int bits, int8_t *q, float *d_out)
             amax = a;
     }
     int ties = 0;
-    if (amax == 0.0f) {
-        *d_out = 0.0f;
+    float d = amax / qmaxf;
+    *d_out = d;
+    if (d == 0.0f) {
         for (int i = 0; i < QK; i++)
             q[i] = 0;
         return 0;
     }
-    float d = amax / qmaxf;
-    *d_out = d;
     for (int i = 0; i < QK; i++) {
         float r = v[i] / d;
         if (r - floorf(r) == 0.5f)

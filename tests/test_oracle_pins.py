@@ -196,6 +196,31 @@ def test_quantize_zero_block():
     assert np.all(q[1, :32] == 0) and d[1, 0] == 0 and d[1, 1] > 0
 
 
+def test_quantize_subnormal_blocks():
+    """Blocks of subnormal values, against numpy's own IEEE float32 arithmetic
+    (subnormals kept): a constant block of the smallest subnormal rotates to
+    fp32(32 a * c) in element 0, whose scale fp32(v0 / 7) is still nonzero; a
+    spike of 7 times it rotates to +-2^-149 everywhere, whose amax / 7 underflows
+    to 0, and a zero scale gives codes 0 (both widths)."""
+    tiny = np.float32(2.0 ** -149)
+    c = np.float32(oracle.inv_sqrt32_f32())
+    x = np.full((1, 32), tiny, dtype=np.float32)
+    q, d, _ = oracle.quantize(x, 4)
+    v0 = np.float32(np.float32(32 * tiny) * c)
+    d0 = np.float32(v0 / np.float32(7.0))
+    assert v0 > 0 and d0 > 0 and d[0, 0] == d0
+    expect = np.zeros(32, dtype=np.int8)
+    expect[0] = np.rint(np.float32(v0 / d0))
+    assert np.array_equal(q[0], expect)
+    x = np.zeros((1, 32), dtype=np.float32)
+    x[0, 8] = np.float32(-7.0) * tiny
+    for bits in (4, 8):
+        q, d, _ = oracle.quantize(x, bits)
+        assert np.float32(np.float32(7.0 * tiny) * c) == tiny   # every |v| = 2^-149
+        assert np.float32(tiny / np.float32(7.0)) == 0.0        # the scale underflows
+        assert d[0, 0] == 0.0 and np.all(q[0] == 0)
+
+
 def test_rint_ties_to_even():
     rows = [ln.split() for ln in open(os.path.join(GOLDEN, "rint_ties.txt"))
             if ln.strip() and not ln.startswith("#")]
