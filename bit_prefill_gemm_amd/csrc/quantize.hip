@@ -14,7 +14,8 @@
 // The stage order is 1,2,4,8,16 and every stage gives the lower index a+b and
 // the upper a-b, each one fp32 rounding; then every value is multiplied by
 // fp32(1/sqrt(32)).  The block scale is amax/7 (8-bit route: amax/127) by
-// IEEE division and the code is rint(v/d) with ties to even, clamped.
+// IEEE division and the code is rint(v/d) with ties to even, clamped; a
+// scale of 0 (an all-zero block, or amax/7 underflowing) gives codes 0.
 //
 // Longer rotations ("Qwen3.8-27B at 45.7 tok/s: DFlash2 in 1bit serve, and
 // 4-bit activations with a Hadamard rotation", section "What's next": larger
@@ -154,7 +155,9 @@ __device__ __forceinline__ void quantize_block(float (&v)[8], int t, int rot, in
 
     constexpr float kQmax = BITS == 4 ? 7.0f : 127.0f;
     constexpr float kQmin = BITS == 4 ? -8.0f : -127.0f;
-    const float d = amax == 0.0f ? 0.0f : amax / kQmax;
+    // a scale of 0 (an all-zero block, or amax / kQmax underflowing) gives
+    // codes 0: every code of such a block dequantizes to 0
+    const float d = amax / kQmax;
     // q = rint(v / d) with the IEEE quotient.  The quotient is first taken as
     // v * rcp(d): its error is below |v/d| * 3 * 2^-24 <= 2.3e-5 (|v/d| <= 127),
     // so wherever that product lies at least 1e-4 from a half-integer it
@@ -166,7 +169,7 @@ __device__ __forceinline__ void quantize_block(float (&v)[8], int t, int rot, in
 #pragma unroll
     for (int i = 0; i < 8; i++) {
         float r = 0.0f;
-        if (amax != 0.0f) {
+        if (d != 0.0f) {
             r = v[i] * rd;
             if (!fast || fabsf(fabsf(r - rintf(r)) - 0.5f) < 1e-4f)
                 r = v[i] / d;
@@ -301,7 +304,8 @@ __global__ __launch_bounds__(kThreads) void quantize_rows_kernel(
             amax = fmaxf(amax, fabsf(v[r][i]));
         amax = fmaxf(amax, quad_swap<kQuadXor1>(amax));
         amax = fmaxf(amax, quad_swap<kQuadXor2>(amax));
-        // IEEE division; an all-zero block has scale 0
+        // IEEE division; an all-zero block has scale 0, and so has a block
+        // whose amax / kQmax underflows (both get codes 0 below)
         d[r] = amax / kQmax;
     }
     // rint(v / d) with the IEEE quotient, taken first as v * rcp(d): its

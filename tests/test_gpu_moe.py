@@ -139,6 +139,12 @@ def test_swiglu_quantize_edge_values(torch):
     g[4] = np.linspace(-88, 89, inter, dtype=np.float32)
     u[5] = 1e-30             # tiny values
     swiglu_and_check(np.concatenate([g, u], axis=1), inter, 4)
+    # subnormal products: scales that underflow to 0 (codes 0) and that do not
+    g2, u2 = g.copy(), u.copy()
+    g2[0], u2[0] = 1e-22, 1e-22
+    g2[1, :32], u2[1, :32] = 1.0, np.float32(2.0 ** -149)
+    for bits in (4, 8):
+        swiglu_and_check(np.concatenate([g2, u2], axis=1), inter, bits)
     # a leading dimension past the two projections
     wide = np.full((rows, 2 * inter + 64), 1e30, dtype=np.float32)
     wide[:, :inter], wide[:, inter:2 * inter] = g, u

@@ -50,6 +50,11 @@ def test_quantize_edge_cases(torch):
     x[4, 5] = -40.0                              # spike
     x[5, :32] = 0.0
     x[5, 17] = 1e-3                              # one nonzero
+    tiny = np.float32(2.0 ** -149)
+    x[6, :32] = tiny                             # subnormal, nonzero scale
+    x[6, 32:64] = 0.0
+    x[6, 40] = -7 * tiny                         # the scale underflows to 0
+    x[6, 64:96] *= np.float32(1e-40)             # subnormal inputs
     for bits in (4, 8):
         quantize_and_check(x, bits)
         quantize_and_check(x[:1], bits)          # M = 1
