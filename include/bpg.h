@@ -41,7 +41,9 @@
  *     may be NULL (nothing is read or written);
  *   - K (input channels) is a multiple of 32, N (output channels) a multiple
  *     of 32; M (tokens) may be 0 (the call is then a no-op after its checks);
- *   - inputs are finite; NaN or Inf input gives unspecified codes.
+ *   - inputs are finite and below 2^120 in magnitude (every sum of the
+ *     rotation, up to 128 values, then stays finite); NaN or Inf input, or a
+ *     rotation that overflows, gives unspecified codes.
  */
 #ifndef BPG_H
 #define BPG_H
