@@ -44,9 +44,11 @@ def sort_and_check(expert_of, tokens, topk, experts):
 
 # entries per thread (of 256): 16 with 16-byte loads kept in registers (512 x 8;
 # 1000 x 4 with a partial last range), 32 with 16-byte loads read twice
-# (1024 x 8), 10 and 1 with 4-byte loads (300 x 8, the small ones)
+# (1024 x 8), 10 and 1 with 4-byte loads (300 x 8, the small ones); the
+# limits: 512 experts, 2^20 entries (4096 per thread)
 @pytest.mark.parametrize("tokens,topk,experts", [(512, 8, 128), (1, 1, 1), (3, 2, 5),
-                                                 (1000, 4, 64), (300, 8, 512), (1024, 8, 128)])
+                                                 (1000, 4, 64), (300, 8, 512), (1024, 8, 128),
+                                                 (131072, 8, 512)])
 def test_route_sort(torch, tokens, topk, experts):
     rng = np.random.default_rng(tokens + topk + experts)
     e, _ = synth.draw_routes(rng, tokens, experts, topk)
