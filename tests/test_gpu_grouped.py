@@ -101,6 +101,18 @@ def test_many_experts_lookup(torch):
     run_grouped(counts, 128, 64, seed=53, rows_extra=80)
 
 
+@pytest.mark.parametrize("E,kernel", [(1024, "expert-slot"), (1025, "grouped 32x128")])
+def test_expert_count_limit(torch, E, kernel):
+    """The slot table holds 1024 experts (four full chunks of the lookup); one
+    expert more routes to the tiled grouped kernel."""
+    rng = np.random.default_rng(E)
+    counts = rng.integers(0, 3, size=E)
+    blocks = synth.draw_q4_0(rng, (E, 128), 64, 0.005, 0.05)
+    W = bb.rotate_pack_weights(blocks, bb.SRC_Q4_0_ROTATED, 128, 64, E)
+    assert bb.w4a4_grouped_gemm_kernel_name(4, int(counts.sum()), W) == kernel
+    run_grouped(counts, 128, 64, seed=E, rows_extra=60)
+
+
 def test_long_k(torch):
     # K = 2^18 (8192 blocks, 1024 stages of two groups per item): the weight
     # image offsets of an expert and the rows' code offsets far from zero
