@@ -55,7 +55,12 @@ def test_quantize_rot_ragged_and_edge(torch, rot):
     x[1, :rot] = 1e-30
     x[2, 5] = 80.0
     x[3, :] = -2.0
+    tiny = np.float32(2.0 ** -149)
+    x[4, :rot] = tiny                 # subnormal inputs
+    x[5, :rot] = 0.0
+    x[5, 3] = -7 * tiny               # a scale that underflows to 0
     quantize_rot_and_check(x, rot, 4)
+    quantize_rot_and_check(x, rot, 8)
     quantize_rot_and_check(np.ascontiguousarray(x[:1]), rot, 4)
     # ldx > k: the left part of a wider matrix
     wide = synth.bf16_bits(rng.standard_normal((9, 4 * rot)).astype(np.float32))

@@ -55,6 +55,10 @@ def test_quantize_unrotated_edge_cases(torch):
     x[1, :32] = -3.0
     x[2, 32:64] = 1e-30
     x[3, 40] = 55.0
+    tiny = np.float32(2.0 ** -149)
+    x[4, :32] = 0.0
+    x[4, 7] = 3 * tiny                # the scale underflows to 0 (no rotation)
+    x[4, 32:64] = 7 * tiny            # subnormal scale, codes 7
     for bits in (4, 8):
         quantize_unrotated_and_check(x, bits)
         quantize_unrotated_and_check(np.ascontiguousarray(x[:1, :32]), bits)
