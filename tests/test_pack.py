@@ -68,7 +68,7 @@ def test_float_source_matches_oracle_bit_exact(dtype):
     w[6, 96:128] = 1e-9                                     # fp16(amax/7) underflows: codes 8
     w[7, :32] = 1e-40                                       # fp32 subnormal weights
     w[8, 32:64] = 0.0
-    w[8, 40] = -2e-7                                        # fp16-subnormal scale
+    w[8, 40] = -2e-5                                        # fp16-subnormal scale
     src = w if dtype == "f32" else synth.bf16_bits(w)
     kind = bb.SRC_F32 if dtype == "f32" else bb.SRC_BF16
     W = bb.rotate_pack_weights(src, kind, n, k, e)
