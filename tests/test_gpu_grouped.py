@@ -8,9 +8,9 @@ than compute units, gathered rows with repeats, repeat runs, and offsets that
 break the ordering rule (accesses stay in bounds; rows that exactly one
 expert owns are still right).
 
-Bar: within 1e-3 row-L2 of the oracle's fp64 output on the same codes (and
-within 2e-5, the fp32 accumulation error); gathered rows bit-identical to the
-same product on explicitly permuted rows.
+Bar: within 1e-3 row-L2 of the oracle's fp64 output on the same codes, and
+every compared element within the fp32 accumulation bound; gathered rows
+bit-identical to the same product on explicitly permuted rows.
 """
 import numpy as np
 import pytest
