@@ -730,10 +730,6 @@ hipError_t launch_dense_bits(int kernel, const GemmProblem &p, hipStream_t strea
 }
 
 // Grouped: 32-row slots (row tiles past an expert's rows are skipped) and
-// 128 columns per workgroup: four waves of 32 x 32, each over the whole of K
-// (an expert's K is short, so splitting it across waves would leave each wave
-// too few blocks to amortise its set-up and the final reduction).
-// Grouped: 32-row slots (row tiles past an expert's rows are skipped) and
 // 128, 64 or 32 columns per workgroup: four waves of 32 x 32, each over the
 // whole of K (an expert's K is short, so splitting it across waves would leave
 // each wave too few blocks to amortise its set-up and the final reduction).
