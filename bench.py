@@ -491,6 +491,20 @@ def summary(res):
             "epilogue_valu_frac": res["epilogue_valu"]["frac"]}
 
 
+def ffn_pair(configs, bits, m=512):
+    """The FFN block's prompt rate from its two measured shapes: quantize X1,
+    the gate and up products (one shape, measured once), quantize X2, the
+    down product; each term the kernel's own graph-timed figure."""
+    g, d = configs.get("ffn512_gate/%d" % bits), configs.get("ffn512_down/%d" % bits)
+    if g is None or d is None:
+        return None
+    us = g["quant_us"] + 2.0 * g["gemm_us"] + d["quant_us"] + d["gemm_us"]
+    return {"us_per_block": us, "tokens_per_s": m / (us * 1e-6),
+            "terms_us": {"quantize_x1": g["quant_us"], "gate": g["gemm_us"],
+                         "up": g["gemm_us"], "quantize_x2": d["quant_us"],
+                         "down": d["gemm_us"]}}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -545,6 +559,10 @@ def main():
                 r, _ = run_gemm(name, bits, "f32", args.config_steps, args.config_warmup,
                                 args.cold_bytes, cache)
             configs["%s/%d" % (name, bits)] = summary(r)
+        for bits in (4, 8):
+            pair = ffn_pair(configs, bits)
+            if pair is not None:
+                configs["ffn512_block/%d" % bits] = pair
         out["configs"] = configs
     if not args.no_cpu_baseline:
         if wl.get("layer"):

@@ -39,3 +39,13 @@ def test_default_workload_is_the_attention_projection():
         assert bench.parse().workload == "attn512"
     finally:
         sys.argv = args
+
+
+def test_ffn_block_rate_sums_its_kernels():
+    # combined rate of the FFN pair: q(X1) + gate + up + q(X2) + down
+    configs = {"ffn512_gate/4": {"quant_us": 6.0, "gemm_us": 140.0},
+               "ffn512_down/4": {"quant_us": 10.0, "gemm_us": 120.0}}
+    pair = bench.ffn_pair(configs, 4)
+    assert pair["us_per_block"] == 6.0 + 2 * 140.0 + 10.0 + 120.0
+    assert abs(pair["tokens_per_s"] - 512 / 416e-6) < 1e-6
+    assert bench.ffn_pair(configs, 8) is None
