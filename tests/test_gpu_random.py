@@ -1,0 +1,118 @@
+"""Seeded random shapes through every routed product, against the oracle.
+
+The hand-picked cases of the other files pin each kernel's edges; these draw
+(M, K, N, code width, input dtype) at random over the shapes the routing sends
+to the weight-stream, tiled, strip and wide kernels, and ragged expert counts
+(empty experts included) for the grouped product, at sizes the oracle computes
+in well under a second.  Every output checked lies within the fp32
+accumulation bound of the oracle's exact value.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from bit_prefill_gemm_amd import binding as bb
+from bit_prefill_gemm_amd import synth
+
+from gpu_util import (act_to_device, assert_within_bound, check_grouped_rows, oracle_codes,
+                      quantize_and_check, row_rel_err, sample_rows, torch_mod, weights_to_device)
+
+pytestmark = pytest.mark.gpu
+
+SEED = 20260
+DENSE_CASES = 80
+GROUPED_CASES = 24
+TOL = 1e-3  # row-L2 relative error, the contract
+
+
+@pytest.fixture(scope="module")
+def torch():
+    t = torch_mod()
+    if not t.cuda.is_available():
+        pytest.skip("no GPU")
+    return t
+
+
+def dense_shape(rng, i):
+    """(m, k, n, bits, dtype): few rows, medium and many rows; N any multiple
+    of 32, of 128 (strips) or of 160 (wide tiles); every fourth case a wide-
+    tile shape (many 64 x 160 tiles, short K)."""
+    bits = int(rng.choice([4, 8]))
+    kind = int(rng.integers(3))
+    m = (int(rng.integers(1, 33)) if kind == 0 else
+         int(rng.integers(33, 160)) if kind == 1 else int(rng.integers(160, 700)))
+    k = 32 * int(rng.integers(1, 97))
+    nk = int(rng.integers(3))
+    n = (32 * int(rng.integers(1, 49)) if nk == 0 else
+         128 * int(rng.integers(1, 13)) if nk == 1 else 160 * int(rng.integers(1, 11)))
+    if i % 4 == 3:
+        m, n, k, bits = (int(rng.integers(65, 400)), 160 * int(rng.integers(32, 128)),
+                         32 * int(rng.integers(1, 8)), 4)
+    while m * k * n > 4e8:
+        m = max(1, m // 2)
+    return m, k, n, bits, str(rng.choice(["f32", "bf16"]))
+
+
+def test_random_dense_shapes(torch):
+    rng = np.random.default_rng(SEED)
+    seen = set()
+    for i in range(DENSE_CASES):
+        m, k, n, bits, dt = dense_shape(rng, i)
+        sd = int(rng.integers(1 << 30))
+        case = synth.small_dense(m, k, n, seed=sd, dtype=dt)
+        codes, scales, q, d = quantize_and_check(case["x"], bits)
+        W = weights_to_device(case["w"], n, k)
+        kname = bb.w4a4_gemm_kernel_name(bits, m, W)
+        print("random dense", i, (m, k, n), bits, dt, kname, flush=True)
+        seen.add(kname)
+        y = bb.w4a4_gemm(codes, scales, bits, W)
+        torch.cuda.synchronize()
+        w, dw = oracle.q4_0_decode(case["w"], k)
+        rows = np.arange(m) if m <= 64 else sample_rows(m, 24, sd)
+        ref = np.concatenate([oracle.gemm_rect(q, d, w, dw, r, r + 1, 0, n) for r in rows])
+        a = np.concatenate([oracle.gemm_abs_rect(q, d, w, dw, r, r + 1, 0, n) for r in rows])
+        yg = y.cpu().numpy()[rows]
+        assert row_rel_err(yg, ref) <= TOL
+        assert_within_bound(yg, ref, a, k, "random dense %d %s" % (i, (m, k, n, bits)))
+    # the draw reaches every dense kernel family
+    assert {"weight-stream", "strip 32x128", "wide 64x160"} <= seen, seen
+    assert any(s.startswith("tiled") for s in seen), seen
+
+
+def test_random_grouped_shapes(torch):
+    rng = np.random.default_rng(SEED + 1)
+    seen = set()
+    for i in range(GROUPED_CASES):
+        E = int(rng.integers(1, 80))
+        counts = rng.integers(0, 90, size=E)
+        counts[rng.random(E) < 0.2] = 0
+        if counts.sum() == 0:
+            counts[0] = 5
+        n = int(rng.choice([64, 96, 128, 256, 384, 512, 768]))
+        k = 32 * int(rng.integers(1, 65))
+        if counts.sum() * k * n > 4e8:
+            k = 32 * max(1, int(4e8 / (counts.sum() * n * 32)))
+        sd = int(rng.integers(1 << 30))
+        off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+        total = int(off[-1])
+        r2 = np.random.default_rng(sd)
+        x, _ = synth.draw_activations(r2, total, k, "normal", 0.02, 20.0)
+        blocks = synth.draw_q4_0(r2, (E, n), k, 0.005, 0.05)
+        codes, scales = bb.quantize_act_h32(act_to_device(x), 4)
+        q, d, _ = oracle.quantize(x, 4)
+        torch.cuda.synchronize()
+        assert np.array_equal(codes.cpu().numpy(), oracle_codes(q, 4))
+        W = bb.rotate_pack_weights(blocks, bb.SRC_Q4_0_ROTATED, n, k, E).to("cuda")
+        wq, dwq = oracle.q4_0_decode(blocks.reshape(E * n, k // 32, 18), k)
+        kname = bb.w4a4_grouped_gemm_kernel_name(4, total, W)
+        print("random grouped", i, E, total, n, k, kname, flush=True)
+        seen.add(kname)
+        y = torch.full((total, n), float("nan"), device="cuda")
+        bb.w4a4_grouped_gemm(codes, scales, 4, torch.from_numpy(off).cuda(), W, y=y)
+        torch.cuda.synchronize()
+        firsts = off[:-1][off[1:] > off[:-1]]
+        lasts = off[1:][off[1:] > off[:-1]] - 1
+        rows = np.unique(np.concatenate([firsts, lasts, sample_rows(total, 30, sd)]))
+        check_grouped_rows(y.cpu().numpy()[rows], q, d, off, wq.reshape(E, n, k),
+                           dwq.reshape(E, n, k // 32), rows, k, "random grouped %d" % i, TOL)
+    assert "expert-slot" in seen and any(s.startswith("grouped") for s in seen), seen
