@@ -3,7 +3,7 @@
 The hand-picked cases of the other files pin each kernel's edges; these draw
 (M, K, N, code width, input dtype) at random over the shapes the routing sends
 to the weight-stream, tiled, strip and wide kernels, and ragged expert counts
-(empty experts included) for the grouped product, at sizes the oracle computes
+(empty experts included) for the grouped product with 4- and 8-bit codes, at sizes the oracle computes
 in well under a second.  Every output checked lies within the fp32
 accumulation bound of the oracle's exact value.
 """
@@ -92,23 +92,24 @@ def test_random_grouped_shapes(torch):
         k = 32 * int(rng.integers(1, 65))
         if counts.sum() * k * n > 4e8:
             k = 32 * max(1, int(4e8 / (counts.sum() * n * 32)))
+        bits = int(rng.choice([4, 4, 8]))
         sd = int(rng.integers(1 << 30))
         off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
         total = int(off[-1])
         r2 = np.random.default_rng(sd)
         x, _ = synth.draw_activations(r2, total, k, "normal", 0.02, 20.0)
         blocks = synth.draw_q4_0(r2, (E, n), k, 0.005, 0.05)
-        codes, scales = bb.quantize_act_h32(act_to_device(x), 4)
-        q, d, _ = oracle.quantize(x, 4)
+        codes, scales = bb.quantize_act_h32(act_to_device(x), bits)
+        q, d, _ = oracle.quantize(x, bits)
         torch.cuda.synchronize()
-        assert np.array_equal(codes.cpu().numpy(), oracle_codes(q, 4))
+        assert np.array_equal(codes.cpu().numpy(), oracle_codes(q, bits))
         W = bb.rotate_pack_weights(blocks, bb.SRC_Q4_0_ROTATED, n, k, E).to("cuda")
         wq, dwq = oracle.q4_0_decode(blocks.reshape(E * n, k // 32, 18), k)
-        kname = bb.w4a4_grouped_gemm_kernel_name(4, total, W)
-        print("random grouped", i, E, total, n, k, kname, flush=True)
+        kname = bb.w4a4_grouped_gemm_kernel_name(bits, total, W)
+        print("random grouped", i, E, total, n, k, bits, kname, flush=True)
         seen.add(kname)
         y = torch.full((total, n), float("nan"), device="cuda")
-        bb.w4a4_grouped_gemm(codes, scales, 4, torch.from_numpy(off).cuda(), W, y=y)
+        bb.w4a4_grouped_gemm(codes, scales, bits, torch.from_numpy(off).cuda(), W, y=y)
         torch.cuda.synchronize()
         firsts = off[:-1][off[1:] > off[:-1]]
         lasts = off[1:][off[1:] > off[:-1]] - 1
