@@ -117,3 +117,65 @@ def test_random_grouped_shapes(torch):
         check_grouped_rows(y.cpu().numpy()[rows], q, d, off, wq.reshape(E, n, k),
                            dwq.reshape(E, n, k // 32), rows, k, "random grouped %d" % i, TOL)
     assert "expert-slot" in seen and any(s.startswith("grouped") for s in seen), seen
+
+
+def test_random_expert_glue(torch):
+    """Random token counts, expert counts and widths through the expert
+    layer's glue: the expert sort (bit-exact), the gathered grouped product
+    (within the fp32 bound), SwiGLU -> rotate -> quantize (bit-exact codes and
+    scales) and the weighted combine (bit-exact)."""
+    rng = np.random.default_rng(SEED + 2)
+    for i in range(16):
+        experts = int(rng.integers(1, 513))
+        topk = int(rng.integers(1, min(8, experts) + 1))
+        tokens = int(rng.integers(1, 400))
+        e_of, w_route = synth.draw_routes(rng, tokens, experts, topk)
+        print("random glue", i, tokens, topk, experts, flush=True)
+        ed = torch.from_numpy(e_of).cuda()
+        off, row_token, slot_of = bb.moe_route_sort(ed, tokens, topk, experts)
+        torch.cuda.synchronize()
+        ref_off, ref_entry, ref_slot = oracle.route_sort(e_of, experts)
+        assert np.array_equal(off.cpu().numpy(), ref_off)
+        assert np.array_equal(row_token.cpu().numpy(), ref_entry // topk)
+        assert np.array_equal(slot_of.cpu().numpy(), ref_slot)
+
+        # the gathered product over these routes (experts with rows only)
+        if experts <= 64:
+            bits = int(rng.choice([4, 8]))
+            n = int(rng.choice([64, 96, 128, 256, 384]))
+            k = 32 * int(rng.integers(1, 33))
+            x, _ = synth.draw_activations(rng, tokens, k, "normal")
+            x = synth.bf16_bits(x)
+            blocks = synth.draw_q4_0(rng, (experts, n), k, 0.002, 0.02)
+            codes, scales = bb.quantize_act_h32(act_to_device(x), bits)
+            q, d, _ = oracle.quantize(x, bits)
+            W = bb.rotate_pack_weights(blocks, bb.SRC_Q4_0_ROTATED, n, k, experts).to("cuda")
+            wq, dwq = oracle.q4_0_decode(blocks.reshape(experts * n, k // 32, 18), k)
+            y = bb.w4a4_grouped_gemm_gather(codes, scales, bits, row_token, off, W)
+            torch.cuda.synchronize()
+            rows = sample_rows(tokens * topk, 24, i)
+            rt = row_token.cpu().numpy()
+            check_grouped_rows(y.cpu().numpy()[rows], q[rt], d[rt], ref_off,
+                               wq.reshape(experts, n, k), dwq.reshape(experts, n, k // 32),
+                               rows, k, "random gather %d" % i, TOL)
+
+        # SwiGLU -> quantize on the routed rows' width
+        inter = 32 * int(rng.integers(1, 65))
+        sbits = int(rng.choice([4, 8]))
+        gu = np.concatenate([(rng.standard_normal((tokens * topk, inter)) * 3.0),
+                             rng.standard_normal((tokens * topk, inter))],
+                            axis=1).astype(np.float32)
+        c2, s2 = bb.swiglu_quantize_h32(torch.from_numpy(gu).cuda(), inter, sbits)
+        torch.cuda.synchronize()
+        q2, d2, _ = oracle.swiglu_quantize(gu, inter, sbits)
+        assert np.array_equal(c2.cpu().numpy(), oracle_codes(q2, sbits))
+        assert np.array_equal(s2.cpu().numpy().view(np.uint32), d2.view(np.uint32))
+
+        # weighted combine of the sorted rows back to tokens
+        hidden = 4 * int(rng.integers(1, 513))
+        dn = rng.standard_normal((tokens * topk, hidden)).astype(np.float32)
+        yc = bb.moe_combine(torch.from_numpy(dn).cuda(), slot_of,
+                            torch.from_numpy(w_route).cuda(), tokens, topk)
+        torch.cuda.synchronize()
+        ref = oracle.moe_combine(dn, ref_slot, w_route, tokens, topk)
+        assert np.array_equal(yc.cpu().numpy().view(np.uint32), ref.view(np.uint32))
