@@ -139,7 +139,7 @@ def test_random_expert_glue(torch):
         assert np.array_equal(row_token.cpu().numpy(), ref_entry // topk)
         assert np.array_equal(slot_of.cpu().numpy(), ref_slot)
 
-        # the gathered product over these routes (experts with rows only)
+        # the gathered product over these routes (up to 64 experts: small weights)
         if experts <= 64:
             bits = int(rng.choice([4, 8]))
             n = int(rng.choice([64, 96, 128, 256, 384]))
