@@ -179,3 +179,61 @@ def test_random_expert_glue(torch):
         torch.cuda.synchronize()
         ref = oracle.moe_combine(dn, ref_slot, w_route, tokens, topk)
         assert np.array_equal(yc.cpu().numpy().view(np.uint32), ref.view(np.uint32))
+
+
+def test_random_route_variants(torch):
+    """Random shapes through the unrotated route and the longer rotations
+    (spans of 64 and 128 values): codes and scales bit-exact, outputs within
+    the fp32 bound; and the bf16 output, equal to the fp32 output rounded to
+    nearest even."""
+    rng = np.random.default_rng(SEED + 3)
+    for i in range(24):
+        rot = int(rng.choice([0, 64, 128]))
+        span = max(rot, 32)
+        bits = int(rng.choice([4, 8]))
+        m = int(rng.choice([int(rng.integers(1, 33)), int(rng.integers(33, 400))]))
+        k = span * int(rng.integers(1, max(2, 2048 // span)))
+        n = int(rng.choice([32 * int(rng.integers(1, 33)), 128 * int(rng.integers(1, 9)),
+                            160 * int(rng.integers(1, 9))]))
+        sd = int(rng.integers(1 << 30))
+        r2 = np.random.default_rng(sd)
+        x, _ = synth.draw_activations(r2, m, k, "normal", 0.02, 20.0)
+        w = synth.draw_weights_f32(r2, n, k, 0.02)
+        print("random route", i, rot, bits, (m, k, n), flush=True)
+        xd = act_to_device(x)
+        if rot == 0:
+            codes, scales = bb.quantize_act_unrotated(xd, bits)
+            q, d, _ = oracle.quantize(x, bits, rotate=False)
+            W = bb.pack_weights_unrotated(w, bb.SRC_F32, n, k).to("cuda")
+            y = bb.w4a4_gemm_unrotated(codes, scales, bits, W)
+            wq, dw = oracle.q4_0_decode(oracle.quantize_weights_q4_0(w, rotate=False), k)
+        else:
+            codes, scales = bb.quantize_act_rot(xd, rot, bits)
+            q, d, _ = oracle.quantize_rot(x, rot, bits)
+            W = bb.rotate_pack_weights_rot(w, bb.SRC_F32, n, k, rot).to("cuda")
+            y = bb.w4a4_gemm_rot(codes, scales, bits, rot, W)
+            wq, dw = oracle.q4_0_decode(oracle.quantize_weights_q4_0_rot(w, rot), k)
+        torch.cuda.synchronize()
+        assert np.array_equal(codes.cpu().numpy(), oracle_codes(q, bits))
+        assert np.array_equal(scales.cpu().numpy().view(np.uint32), d.view(np.uint32))
+        rows = np.arange(m) if m <= 32 else sample_rows(m, 16, sd)
+        ref = np.concatenate([oracle.gemm_rect(q, d, wq, dw, r, r + 1, 0, n) for r in rows])
+        a = np.concatenate([oracle.gemm_abs_rect(q, d, wq, dw, r, r + 1, 0, n) for r in rows])
+        yg = y.cpu().numpy()[rows]
+        assert row_rel_err(yg, ref) <= TOL
+        assert_within_bound(yg, ref, a, k, "random route %d" % i)
+    rng = np.random.default_rng(SEED + 4)
+    for i in range(12):
+        bits = int(rng.choice([4, 8]))
+        m = int(rng.choice([int(rng.integers(1, 33)), int(rng.integers(33, 600))]))
+        k = 32 * int(rng.integers(1, 65))
+        n = int(rng.choice([32 * int(rng.integers(1, 33)), 128 * int(rng.integers(1, 17)),
+                            160 * int(rng.integers(1, 33))]))
+        case = synth.small_dense(m, k, n, seed=int(rng.integers(1 << 30)), dtype="bf16")
+        print("random bf16 out", i, bits, (m, k, n), flush=True)
+        codes, scales = bb.quantize_act_h32(act_to_device(case["x"]), bits)
+        W = weights_to_device(case["w"], n, k)
+        y32 = bb.w4a4_gemm(codes, scales, bits, W)
+        y16 = bb.w4a4_gemm_bf16(codes, scales, bits, W)
+        torch.cuda.synchronize()
+        assert torch.equal(y16.view(torch.int16), y32.to(torch.bfloat16).view(torch.int16))
