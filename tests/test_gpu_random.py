@@ -1,11 +1,17 @@
 """Seeded random shapes through every routed product, against the oracle.
 
 The hand-picked cases of the other files pin each kernel's edges; these draw
-(M, K, N, code width, input dtype) at random over the shapes the routing sends
-to the weight-stream, tiled, strip and wide kernels, and ragged expert counts
-(empty experts included) for the grouped product with 4- and 8-bit codes, at sizes the oracle computes
-in well under a second.  Every output checked lies within the fp32
-accumulation bound of the oracle's exact value.
+shapes at random:
+  - (M, K, N, code width, input dtype) over the shapes the routing sends to the
+    weight-stream, tiled, strip and wide kernels;
+  - ragged expert counts (empty experts included) for the grouped product with
+    4- and 8-bit codes;
+  - token, expert and width counts through the expert layer's sort, gathered
+    product, SwiGLU-quantize and combine;
+  - the unrotated route, the longer rotations and the bf16 output.
+All at sizes the oracle computes in well under a second.  Codes, scales, sort
+indices and combines are compared bit for bit; every product output checked
+lies within the fp32 accumulation bound of the oracle's exact value.
 """
 import numpy as np
 import pytest
