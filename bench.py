@@ -184,13 +184,19 @@ def timed_steps(torch, stream, step, steps, warmup, copies):
 
 
 def graph_time_us(torch, stream, launch, n=GRAPH_LAUNCHES, replays=GRAPH_REPLAYS):
+    """The median of graph_time_spread_us."""
+    return graph_time_spread_us(torch, stream, launch, n, replays)[0]
+
+
+def graph_time_spread_us(torch, stream, launch, n=GRAPH_LAUNCHES, replays=GRAPH_REPLAYS):
     """Per-launch duration of launch(0), ..., launch(n-1) on `stream`, replayed
     from one captured graph: the kernels run back to back with no host work and
     no event packets between them, so the time between the two events around a
     replay, divided by n, is one kernel's duration plus one dispatch gap.  (An
     event pair around each launch instead adds the cost of its two packets to
     every launch, several microseconds, which dominates a short kernel.)  The
-    median over `replays` replays after one untimed replay."""
+    median over `replays` replays after one untimed replay, with the fastest and
+    the slowest of them: (median, min, max)."""
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=stream):
         for i in range(n):
@@ -208,7 +214,7 @@ def graph_time_us(torch, stream, launch, n=GRAPH_LAUNCHES, replays=GRAPH_REPLAYS
             ts.append(e0.elapsed_time(e1) * 1e3 / n)
     torch.cuda.synchronize()
     del g
-    return float(np.median(ts))
+    return float(np.median(ts)), float(min(ts)), float(max(ts))
 
 
 def parse():
@@ -431,7 +437,8 @@ def run_gemm(workload, bits, out_kind, steps, warmup, cold_bytes, cache):
     # Each kernel's own duration is taken afterwards from a graph replay of
     # back-to-back launches over the same cold copies (graph_time_us).
     ms_per_step, eager_ms = timed_steps(torch, stream, step, steps, warmup, copies)
-    gemm_ms = graph_time_us(torch, stream, lambda i: gemm(i % copies)) * 1e-3
+    gemm_spread = graph_time_spread_us(torch, stream, lambda i: gemm(i % copies))
+    gemm_ms = gemm_spread[0] * 1e-3
     quant_ms = graph_time_us(torch, stream, lambda i: quantize(i % copies)) * 1e-3
     # whole steps replayed the same way: the product right after the quantizer
     # that wrote its codes runs a few percent longer than back to back
@@ -459,6 +466,7 @@ def run_gemm(workload, bits, out_kind, steps, warmup, cold_bytes, cache):
         "eff_TOPS": eff_tops,
         "pct_int8_peak": 100.0 * eff_tops / (PEAK_INT8_OPS / 1e12),
         "gemm_us": gemm_ms * 1e3,
+        "gemm_us_min_max": [gemm_spread[1], gemm_spread[2]],
         "quant_us": quant_ms * 1e3,
         "step_graph_us": step_graph_ms * 1e3,
         "gemm_in_step_us": (step_graph_ms - quant_ms) * 1e3,
@@ -481,7 +489,8 @@ def summary(res):
                 "tokens_per_s": res["value"],
                 "kernel_us": res["kernel_us"], "roofline": res["roofline"]}
     r = res["roofline"]
-    return {"kernel": res["kernel"], "gemm_us": res["gemm_us"], "quant_us": res["quant_us"],
+    return {"kernel": res["kernel"], "gemm_us": res["gemm_us"],
+            "gemm_us_min_max": res["gemm_us_min_max"], "quant_us": res["quant_us"],
             "gemm_in_step_us": res["gemm_in_step_us"],
             "step_us": res["step_us"], "eager_step_us": res["eager_step_us"],
             "tokens_per_s": res["value"],
